@@ -1,0 +1,31 @@
+"""CPU oracle for MLA absorbed decode -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and it imports nothing
+from the product path: it shares no code, tables or helpers with the kernels.
+
+The oracle computes the plain, non-absorbed definition of one decode step:
+rebuild every cached token's per-head key [W_UK c ; k_R] and value W_UV c
+explicitly, then run ordinary softmax attention for the single new query with
+scale 1/sqrt(d_h + d_R).  Arithmetic is float64 unless a caller asks for
+float32.
+
+Parity status of each function (what pins it, see tests/test_oracle_pins.py):
+  expand_kv        pinned: worked example of "MLA storage: Representing KV with
+                   a small latent vector" (keys [1,2],[2,3]; values [4,2],[1,5]).
+  attend / decode  pinned: closed forms (one token, zero query, two tokens),
+                   torch scaled_dot_product_attention on explicit K/V, the
+                   absorption identities of "Grouped-query and latent attention".
+  merge_partials   pinned: equals one-pass softmax for every split of the tokens.
+  cache_size.*     pinned: every cache-size figure printed on the pages.
+  decode_bf16 / decode_e4m3  pinned: OCP FP8 special values, bf16 bit patterns.
+  The rotary pairing convention of the input generator is not fixed by the
+  pages: parity unpinned for that convention (both sides consume the same
+  already-rotated bytes, so parity does not depend on it).
+"""
+from .mla_decode import (  # noqa: F401
+    decode_bf16, decode_e4m3, gather_rows, expand_kv, attend, decode,
+    merge_partials, relative_l2,
+)
+from . import cache_size  # noqa: F401
