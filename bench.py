@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of one absorbed MLA decode step on one MI355X.
+
+A step is the whole hot path on one batch: mla_absorb_q -> mla_decode_attn (partial pass +
+combine pass) -> mla_uv_out, over inputs already resident in HBM.  Prints one JSON line.
+
+Default workload: DeepSeek-V3-shape decode, B=1, H=128, d_c=512, d_R=64, N=4096 cached tokens,
+bf16 caches and weights (``--config 3/4/5`` selects the other synthetic workloads).
+
+Timing: inputs are replicated into enough copies that consecutive steps never find their
+weights or cache in the 256 MB Infinity Cache (about 1 GB rotated); one HIP graph holds one step
+per copy and is replayed, so host launch overhead is not timed.  Per-kernel durations come from
+HIP events recorded around each kernel on the stream the kernels run on, after the stream has
+been primed so that the host runs ahead of the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "cached latents/sec + achieved HBM TB/s, MLA absorbed decode (V3 shape)"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "k_absorb_bf16": "absorb_uv_mfma.hip",
+    "k_uv_bf16": "absorb_uv_mfma.hip",
+    "k_partial_mfma": "decode_partial_mfma.hip",
+    "k_combine": "decode_generic.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--rotate-mb", type=float, default=1024.0, help="bytes of input copies rotated per pass")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
+    ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(fname: str) -> str:
+    p = os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", fname)
+    with open(p, "rb") as f:
+        h = hashlib.sha256(f.read())
+    with open(os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", "mla_internal.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(wl, sum_len):
+    """Algorithmic HBM bytes per kernel launch (what the method must move)."""
+    B, H, d_h, d_c, d_R = wl.B, wl.H, wl.d_h, wl.d_c, wl.d_R
+    lat_b = {"bf16": 2, "fp8": 1, "f32": 4}[wl.dtype]
+    rope_b = 4 if wl.dtype == "f32" else 2
+    qb = 4 if wl.dtype == "f32" else 2
+    per_tok = d_c * lat_b + d_R * rope_b + (4 if wl.dtype == "fp8" else 0)
+    absorb = H * d_h * d_c * qb + B * H * d_h * qb + B * H * d_c * qb
+    partial = sum_len * per_tok + B * H * (d_c + d_R) * qb
+    combine = B * H * d_c * 4 + B * H * 4
+    uv = H * d_h * d_c * qb + B * H * d_c * 4 + B * H * d_h * 4
+    return {"absorb": absorb, "partial": partial, "combine": combine, "uv": uv}, per_tok
+
+
+def alg_flops(wl, sum_len):
+    B, H, d_h, d_c, d_R = wl.B, wl.H, wl.d_h, wl.d_c, wl.d_R
+    return {"absorb": 2 * B * H * d_h * d_c,
+            "partial": sum_len * (2 * H * (d_c + d_R) + 2 * H * d_c),
+            "combine": 0, "uv": 2 * B * H * d_h * d_c}
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle as it stands, on this host's cores, timed on whole steps of the workload (or on
+    a bounded sample of sequences when one step would exceed the budget)."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(limits=cores):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        wl = inp.wl
+        # sample: all heads of a prefix of the sequences, grown until the budget is used
+        order = list(range(wl.B))
+        done_lat, t_used, reps = 0, 0.0, 0
+        nb = 1
+        while t_used < budget_s:
+            bs = order[:nb]
+            pairs = [(b, h) for b in bs for h in range(wl.H)]
+            t0 = time.perf_counter()
+            oracle.decode(inp, pairs=pairs, want_diag=False)
+            dt = time.perf_counter() - t0
+            t_used += dt
+            done_lat += int(inp.lens[bs].astype(np.int64).sum())
+            reps += 1
+            if dt < budget_s / 8 and nb < wl.B:
+                nb = min(wl.B, nb * 2)
+        sample = (f"{reps} oracle runs over the first {nb} of {wl.B} sequences (all {wl.H} heads; explicit K/V "
+                  f"rebuild, float64 numpy), {t_used:.1f} s")
+        return {"value": done_lat / t_used, "unit": "latents/s", "cores": threads, "kind": "oracle",
+                "sample": sample}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the absorbed decode kernel is measured "
+                                   "on one MI355X; multi-GPU sharding is a design note, not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_attn_amd import ops
+    from mla_latent_kv_attn_amd.step import DecodeStep
+    from workloads import make_inputs
+    from workloads.configs import WORKLOADS
+    from workloads.device import device_cache, to_device
+
+    wl = WORKLOADS[args.config]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(wl, poison=False)
+    sum_len = inp.sum_len
+    base = to_device(inp, dev)
+    per_copy = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    R = max(1, min(64, math.ceil(args.rotate_mb * 1e6 / per_copy)))
+    copies = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(R - 1)]
+    caches = [device_cache(inp, c) for c in copies]
+    q_dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    step = DecodeStep(wl.B, wl.H, wl.d_h, wl.d_c, wl.d_R, wl.n_max, q_dtype, dev, args.num_splits)
+    W = args.num_splits or ops.mla_decode_auto_splits(wl.B, wl.H, wl.n_max)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB, splits={W}", file=sys.stderr, flush=True)
+
+    def one(i):
+        c = copies[i % R]
+        step(c["q_C"], c["q_R"], c["W_UK"], c["W_UV"], caches[i % R], c["lens"])
+
+    # ---------------- whole-step timing (graph of R steps, replayed)
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, R)):
+            one(i)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(R):
+                one(i)
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(args.steps / R))
+        steps = reps * R
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):          # replay() launches on the current stream
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        e1.synchronize()
+    else:
+        steps = args.steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(steps):
+                one(i)
+            e1.record(stream)
+        e1.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    torch.cuda.synchronize()
+
+    # ---------------- per-kernel durations (HIP events around each launch)
+    names = ["absorb", "partial", "combine", "uv"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.kernel_reps)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(50_000_000)  # keep the GPU busy while the host enqueues everything below
+        for r in range(args.kernel_reps):
+            c = copies[r % R]
+            e = ev[r]
+            e[0].record(stream)
+            ops.mla_absorb_q(c["q_C"], c["W_UK"], out=step.q_abs, stream=stream)
+            e[1].record(stream)
+            ops.mla_decode_partial(step.q_abs, c["q_R"], caches[r % R], c["lens"], wl.n_max, step.scale,
+                                   step.workspace, num_splits=args.num_splits, stream=stream)
+            e[2].record(stream)
+            ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent, step.lse,
+                                   num_splits=args.num_splits, stream=stream)
+            e[3].record(stream)
+            ops.mla_uv_out(step.o_latent, c["W_UV"], out=step.out, stream=stream)
+            e[4].record(stream)
+    torch.cuda.synchronize()
+    kern_us = {n: float(np.mean([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(1, args.kernel_reps)]) * 1e3)
+               for i, n in enumerate(names)}
+
+    ab, per_tok = alg_bytes(wl, sum_len)
+    af = alg_flops(wl, sum_len)
+    step_bytes = sum(ab.values())
+    value = sum_len / (ms_per_step * 1e-3)
+    dom = max(names, key=lambda n: kern_us[n])
+    kname = {"absorb": "k_absorb_bf16", "partial": "k_partial_mfma", "combine": "k_combine", "uv": "k_uv_bf16"}[dom]
+    achieved_gbps = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_profiles(kname, wl.name), "alg_bytes_per_launch": ab[dom],
+                "avg_us": round(kern_us[dom], 3)}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "latents/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else ("fp8-e4m3 latents, bf16 MFMA" if wl.dtype == "fp8" else "f32"),
+        "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
+        "config": {"workload": wl.description, "B": wl.B, "H": wl.H, "d_c": wl.d_c, "d_R": wl.d_R,
+                   "sum_len": sum_len, "layout": wl.layout, "num_splits": W, "graph": use_graph,
+                   "input_copies_rotated": R},
+        "hbm_TBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e12, 3),
+        "step_alg_bytes": step_bytes,
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernels_frac_of_hbm_peak": {k: round(ab[k] / (kern_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4) for k in names},
+        "partial_mfma_util": round(af["partial"] / (kern_us["partial"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def traffic_from_profiles(kname: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if a committed measurement exists for
+    this kernel, this workload and the current kernel source."""
+    path = os.path.join(PROFILES, f"{kname}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(KERNEL_SOURCES[kname]):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) library for the absorbed decode step of
+ * Multi-Head Latent Attention.
+ *
+ * One decode step, per sequence b and head h (column-vector notation of
+ * "Grouped-query and latent attention", sections "Multi-head latent attention
+ * (MLA)", "The absorption trick" and "Why a separate rotary key"):
+ *
+ *   q'[b,h]    = W_UK[h]^T q_C[b,h]                                  mla_absorb_q
+ *   s[b,h,j]   = scale * (q'[b,h] . c[b,j]  +  q_R[b,h] . k_R[b,j])   j < len[b]
+ *   a[b,h,:]   = softmax_j s[b,h,:]
+ *   o_lat[b,h] = sum_j a[b,h,j] c[b,j]                                mla_decode_attn
+ *   o[b,h]     = W_UV[h] o_lat[b,h]                                   mla_uv_out
+ *
+ * c[b,j] is the cached d_c-wide latent of token j and k_R[b,j] the cached,
+ * already rotated d_R-wide rope key shared by all heads ("MLA storage:
+ * Representing KV with a small latent vector", section "Storing a positional
+ * key separately").  scale is 1/sqrt(d_h + d_R).  Full keys and values are
+ * never formed.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *    every buffer.  Tensors are dense row-major with the shapes given, except
+ *    the cache, which is described by mla_cache_desc.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return without synchronising.  They allocate no memory.
+ *  - Host-side argument checks run before anything is enqueued and return a
+ *    status other than MLA_OK; nothing is launched in that case.  A failed
+ *    launch returns MLA_ERR_HIP and mla_last_hip_error() gives the hipError_t
+ *    (per calling thread).
+ *  - Values held in device memory (sequence lengths, block-table entries) are
+ *    not validated: a length above max_len or outside the cache capacity, or a
+ *    page id outside the pool, is undefined behaviour.
+ *  - Results are bitwise reproducible for fixed arguments (no atomics).
+ *  - Calls on different streams are independent; the library keeps no state
+ *    other than the per-thread last HIP error.
+ */
+#ifndef MLA_AMD_MLA_H
+#define MLA_AMD_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+  MLA_ERR_SHAPE = 2,        /* a size is negative, zero where not allowed, or inconsistent */
+  MLA_ERR_DTYPE = 3,        /* unknown dtype or unsupported dtype combination    */
+  MLA_ERR_UNSUPPORTED = 4,  /* valid arguments that this build has no kernel for */
+  MLA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required           */
+  MLA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed        */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,              /* IEEE binary32                                    */
+  MLA_BF16 = 1,             /* bfloat16                                         */
+  MLA_FP8_E4M3 = 2          /* OCP FP8 E4M3 (bias 7, max 448, no infinities, S.1111.111 = NaN) */
+} mla_dtype;
+
+/*
+ * One layer's latent + rope-key cache.  Row j of sequence b:
+ *   contiguous (block_table == NULL):
+ *     latent row  = latent + b*latent_stride_b + j*latent_stride_tok      (elements of latent_dtype)
+ *     rope row    = rope   + b*rope_stride_b   + j*rope_stride_tok        (elements of rope_dtype)
+ *     scale       = latent_scale[b*scale_stride_b + j]                    (FP8 latents only)
+ *   paged (block_table != NULL): with p = block_table[b*max_pages + j/page_size]
+ *   and s = j % page_size, the *_stride_b fields are page strides:
+ *     latent row  = latent + p*latent_stride_b + s*latent_stride_tok
+ *     rope row    = rope   + p*rope_stride_b   + s*rope_stride_tok
+ *     scale       = latent_scale[p*scale_stride_b + s]
+ * The rows of a latent and of a rope key must each be contiguous (unit
+ * element stride).  Latent and rope may live in one packed row [c ; k_R]
+ * (the two stored parts of one illustrated cache row in "MLA storage:
+ * Representing KV with a small latent vector") or in separate buffers.
+ * An FP8 latent c is latent_scale * decode(code).
+ */
+typedef struct mla_cache_desc {
+  const void* latent;
+  const void* rope;
+  const float* latent_scale;   /* FP8 latents only, else NULL */
+  const int32_t* block_table;  /* NULL = contiguous; else [B, max_pages] int32 physical page ids */
+  int32_t latent_dtype;        /* MLA_F32, MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t rope_dtype;          /* MLA_F32 or MLA_BF16 */
+  int64_t latent_stride_b;
+  int64_t latent_stride_tok;
+  int64_t rope_stride_b;
+  int64_t rope_stride_tok;
+  int64_t scale_stride_b;
+  int32_t page_size;           /* paged only: tokens per page */
+  int32_t max_pages;           /* paged only: columns of block_table */
+} mla_cache_desc;
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(int status);
+
+/* hipError_t of the last MLA_ERR_HIP returned on the calling thread (0 if none). */
+int mla_last_hip_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int mla_version(void);
+
+/*
+ * mla_absorb_q -- fold W_UK into the query ("Grouped-query and latent
+ * attention", section "The absorption trick": q' = W_UK^T q_C, computed once
+ * for the new token).
+ *   q_C    [B, H, d_h]   in_dtype
+ *   W_UK   [H, d_h, d_c] in_dtype   (W_UK[h] maps a latent to head h's content key)
+ *   q_abs  [B, H, d_c]   out_dtype  (written)
+ * Dtypes: in MLA_F32 -> out MLA_F32 (any d_h <= 1024, d_c <= 4096), or
+ *         in MLA_BF16 -> out MLA_BF16 (d_h == 128, d_c == 512; fp32 accumulation,
+ *         one round-to-nearest-even to bf16 at the end).
+ * B == 0 is a no-op.
+ */
+int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, int out_dtype,
+                 int B, int H, int d_h, int d_c, void* stream);
+
+/*
+ * Workspace (device bytes) mla_decode_attn needs for these sizes.  num_splits
+ * is the number of partial-pass workgroups over the whole batch (0 = the
+ * library's choice for (B, H, max_len), the same choice mla_decode_attn makes).
+ * Returns 0 for invalid sizes.
+ */
+size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits);
+
+/* The number of partial-pass workgroups mla_decode_attn uses when num_splits == 0. */
+int mla_decode_auto_splits(int B, int H, int max_len);
+
+/*
+ * mla_decode_attn -- scores of the folded query against the cached latents
+ * plus the rope term, scaled softmax over j < seq_lens[b], and the weighted
+ * latent sum ("Grouped-query and latent attention", sections "The absorption
+ * trick" and "Why a separate rotary key"; the attention row of the newest
+ * token only, "The Journey to Multi-Head Latent Attention", section "The KV
+ * cache -- and why it exists at all").
+ *
+ * Two passes on `stream`: a partial pass splits the concatenated token tiles of
+ * the batch evenly over num_splits workgroups, each writing a running
+ * (max, sum, weighted latent sum) per head for every sequence it touches into
+ * the workspace; a combine pass merges those partials per (b, h).
+ *   q_abs     [B, H, d_c]  q_dtype   folded queries (output of mla_absorb_q)
+ *   q_R       [B, H, d_R]  q_dtype   rotated rope queries
+ *   cache     host pointer to the descriptor (read during the call only)
+ *   seq_lens  [B] int32 device: tokens cached per sequence, 0 <= len <= max_len
+ *   max_len   host: an upper bound on every seq_lens[b]
+ *   scale     softmax scale, normally 1/sqrt(d_h + d_R)
+ *   workspace device buffer of at least mla_decode_workspace_bytes(...) bytes,
+ *             any contents; overwritten
+ *   o_latent  [B, H, d_c] float32 (written): sum_j a_j c_j
+ *   lse       [B, H] float32 (written unless NULL): natural-log log-sum-exp of
+ *             the scaled scores
+ * A sequence with len 0 gives o_latent = 0 and lse = -inf.
+ * Supported: q_dtype MLA_F32 with an MLA_F32 cache (d_c <= 1024, d_R <= 256);
+ *            q_dtype MLA_BF16 with an MLA_BF16 or MLA_FP8_E4M3 latent and MLA_BF16
+ *            rope (d_c == 512, d_R == 64, H a multiple of 32 up to 128;
+ *            paged: page_size a multiple of 32).  B <= 2048.
+ */
+int mla_decode_attn(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                    const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, float* o_latent, float* lse,
+                    void* stream);
+
+/*
+ * The two passes of mla_decode_attn as separate calls (same arguments, same workspace contract),
+ * for callers that schedule or time them individually.  mla_decode_attn(...) is exactly
+ * mla_decode_partial(...) followed by mla_decode_combine(...) on the same stream with the same
+ * B, H, d_c, max_len, num_splits and workspace.
+ *   mla_decode_partial: writes one (max, sum, weighted latent sum) partial per head for every
+ *     (workgroup, sequence) segment into the workspace.
+ *   mla_decode_combine: merges the partials of each (b, h) into o_latent and lse (the
+ *     log-sum-exp merge: M = max m_s, L = sum 2^(m_s-M) l_s, o = sum 2^(m_s-M) acc_s / L).
+ */
+int mla_decode_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                       const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
+                       const void* workspace, size_t workspace_bytes, float* o_latent, float* lse, void* stream);
+
+/*
+ * mla_uv_out -- apply W_UV once to the weighted latent sum ("Grouped-query and
+ * latent attention", section "The absorption trick": sum_j a_j W_UV c_j =
+ * W_UV sum_j a_j c_j).
+ *   o_latent [B, H, d_c]  float32
+ *   W_UV     [H, d_h, d_c] w_dtype (MLA_F32, or MLA_BF16 with d_h == 128, d_c == 512)
+ *   out      [B, H, d_h]  float32 (written), fp32 accumulation
+ * B == 0 is a no-op.
+ */
+int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out, int B, int H, int d_h,
+               int d_c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_AMD_MLA_H */

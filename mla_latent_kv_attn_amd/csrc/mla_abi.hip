@@ -1,0 +1,245 @@
+// Host side of the C ABI declared in include/mla.h: argument validation, path selection,
+// workspace sizing and launches.  No device memory is allocated here.
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = (int)e;
+  return MLA_ERR_HIP;
+}
+
+bool known_dtype(int d) { return d == MLA_F32 || d == MLA_BF16 || d == MLA_FP8_E4M3; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Partial-pass workgroups when the caller passes 0: one workgroup per CU for large batches
+// (the kernel runs one workgroup per CU), fewer for short single-sequence work so that each
+// workgroup owns at least four 32-token tiles.
+int auto_splits(int B, int H, int max_len) {
+  (void)H;
+  const int64_t nt = (int64_t)B * ((max_len + mla::kTile - 1) / mla::kTile);
+  int64_t w = nt / 4;
+  if (w > 256) w = 256;
+  if (w < 1) w = 1;
+  return (int)w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: invalid or inconsistent sizes";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown or invalid dtype combination";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for these arguments";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown mla status";
+  }
+}
+
+int mla_last_hip_error(void) { return g_last_hip_error; }
+
+int mla_version(void) { return 10000; }
+
+int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, int out_dtype, int B, int H,
+                 int d_h, int d_c, void* stream) {
+  if (B < 0 || H < 1 || d_h < 1 || d_c < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(in_dtype) || !known_dtype(out_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!q_C || !W_UK || !q_abs) return MLA_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == MLA_F32 && out_dtype == MLA_F32) {
+    if (d_h > 1024 || d_c > 4096) return MLA_ERR_UNSUPPORTED;
+    return hip_status(mla::launch_absorb_f32((const float*)q_C, (const float*)W_UK, (float*)q_abs, B, H, d_h, d_c, s));
+  }
+  if (in_dtype == MLA_BF16 && out_dtype == MLA_BF16) {
+    if (d_h != 128 || d_c != 512) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(q_C) || !aligned16(W_UK)) return MLA_ERR_UNSUPPORTED;
+    return hip_status(mla::launch_absorb_bf16(q_C, W_UK, q_abs, B, H, s));
+  }
+  return MLA_ERR_UNSUPPORTED;
+}
+
+int mla_decode_auto_splits(int B, int H, int max_len) {
+  if (B < 0 || H < 1 || max_len < 0) return 0;
+  return auto_splits(B, H, max_len);
+}
+
+size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits) {
+  if (B < 1 || H < 1 || d_c < 1 || max_len < 0 || num_splits < 0) return 0;
+  const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
+  return mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates the arguments of the partial pass and fills its argument block.  Returns MLA_OK or an
+// error status; *fp8 / *generic report the selected kernel family.
+int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                    const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, mla::PartialArgs* pa, bool* generic,
+                    bool* fp8, bool* paged) {
+  if (B < 0 || H < 1 || d_c < 4 || (d_c % 4) != 0 || d_R < 1 || max_len < 0 || num_splits < 0)
+    return MLA_ERR_SHAPE;
+  if (B > mla::kMaxB) return MLA_ERR_UNSUPPORTED;
+  if (!known_dtype(q_dtype)) return MLA_ERR_DTYPE;
+  if (!cache) return MLA_ERR_NULL;
+  if (!known_dtype(cache->latent_dtype) || !known_dtype(cache->rope_dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(scale)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q_abs || !q_R || !seq_lens || !cache->latent || !cache->rope) return MLA_ERR_NULL;
+  if (cache->latent_stride_tok < 1 || cache->rope_stride_tok < 1 || cache->latent_stride_b < 0 ||
+      cache->rope_stride_b < 0)
+    return MLA_ERR_SHAPE;
+  *paged = cache->block_table != nullptr;
+  if (*paged) {
+    if (cache->page_size < 1 || cache->max_pages < 1) return MLA_ERR_SHAPE;
+    if ((int64_t)cache->max_pages * cache->page_size < (int64_t)max_len) return MLA_ERR_SHAPE;
+  }
+  const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
+  if (W > 65535) return MLA_ERR_SHAPE;
+  const size_t need = mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+
+  if (q_dtype == MLA_F32 && cache->latent_dtype == MLA_F32 && cache->rope_dtype == MLA_F32) {
+    if (d_c > 1024 || d_R > 256) return MLA_ERR_UNSUPPORTED;
+    *generic = true;
+    *fp8 = false;
+  } else if (q_dtype == MLA_BF16 && (cache->latent_dtype == MLA_BF16 || cache->latent_dtype == MLA_FP8_E4M3) &&
+             cache->rope_dtype == MLA_BF16) {
+    *generic = false;
+    *fp8 = cache->latent_dtype == MLA_FP8_E4M3;
+    if (d_c != 512 || d_R != 64 || !(H == 32 || H == 64 || H == 128)) return MLA_ERR_UNSUPPORTED;
+    if (*paged && (cache->page_size % mla::kTile) != 0) return MLA_ERR_UNSUPPORTED;
+    if (*fp8 && !cache->latent_scale) return MLA_ERR_NULL;
+    const int les = *fp8 ? 1 : 2;
+    if (!aligned16(cache->latent) || !aligned16(cache->rope) || !aligned16(q_abs) || !aligned16(q_R) ||
+        ((cache->latent_stride_tok * les) % 16) != 0 || ((cache->latent_stride_b * les) % 16) != 0 ||
+        ((cache->rope_stride_tok * 2) % 16) != 0 || ((cache->rope_stride_b * 2) % 16) != 0 ||
+        (*fp8 && (((uintptr_t)cache->latent_scale & 3u) != 0 || cache->scale_stride_b < 0)))
+      return MLA_ERR_UNSUPPORTED;
+  } else {
+    return MLA_ERR_UNSUPPORTED;
+  }
+
+  pa->q_abs = q_abs;
+  pa->q_R = q_R;
+  pa->latent = cache->latent;
+  pa->rope = cache->rope;
+  pa->lscale = cache->latent_scale;
+  pa->block_table = cache->block_table;
+  pa->lat_sb = cache->latent_stride_b;
+  pa->lat_st = cache->latent_stride_tok;
+  pa->rope_sb = cache->rope_stride_b;
+  pa->rope_st = cache->rope_stride_tok;
+  pa->scale_sb = cache->scale_stride_b;
+  pa->page_size = *paged ? cache->page_size : 1;
+  pa->max_pages = *paged ? cache->max_pages : 0;
+  pa->seq_lens = seq_lens;
+  pa->B = B;
+  pa->H = H;
+  pa->d_c = d_c;
+  pa->d_R = d_R;
+  pa->W = W;
+  pa->sl2 = scale * 1.4426950408889634f;
+  pa->ws_acc = (float*)workspace;
+  pa->ws_ml = (float*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
+  return MLA_OK;
+}
+
+int launch_partial(const mla::PartialArgs& pa, bool generic, bool fp8, bool paged, hipStream_t s) {
+  return hip_status(generic ? mla::launch_partial_f32(pa, s) : mla::launch_partial_mfma(pa, fp8, paged, s));
+}
+
+int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
+                    const void* workspace, size_t workspace_bytes, float* o_latent, float* lse,
+                    mla::CombineArgs* ca) {
+  if (B < 0 || H < 1 || d_c < 4 || (d_c % 4) != 0 || max_len < 0 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (B > mla::kMaxB) return MLA_ERR_UNSUPPORTED;
+  if (B == 0) return MLA_OK;
+  if (!seq_lens || !o_latent) return MLA_ERR_NULL;
+  const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
+  if (W > 65535) return MLA_ERR_SHAPE;
+  const size_t need = mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  ca->seq_lens = seq_lens;
+  ca->B = B;
+  ca->H = H;
+  ca->d_c = d_c;
+  ca->W = W;
+  ca->ws_acc = (const float*)workspace;
+  ca->ws_ml = (const float*)((const char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
+  ca->o_latent = o_latent;
+  ca->lse = lse;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                       const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  mla::PartialArgs pa;
+  bool generic = false, fp8 = false, paged = false;
+  int st = prepare_partial(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, num_splits,
+                           workspace, workspace_bytes, &pa, &generic, &fp8, &paged);
+  if (st != MLA_OK || B == 0) return st;
+  return launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
+}
+
+int mla_decode_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
+                       const void* workspace, size_t workspace_bytes, float* o_latent, float* lse, void* stream) {
+  mla::CombineArgs ca;
+  int st = prepare_combine(seq_lens, max_len, B, H, d_c, num_splits, workspace, workspace_bytes, o_latent, lse, &ca);
+  if (st != MLA_OK || B == 0) return st;
+  return hip_status(mla::launch_combine(ca, (hipStream_t)stream));
+}
+
+int mla_decode_attn(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                    const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, float* o_latent, float* lse,
+                    void* stream) {
+  mla::PartialArgs pa;
+  mla::CombineArgs ca;
+  bool generic = false, fp8 = false, paged = false;
+  int st = prepare_partial(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, num_splits,
+                           workspace, workspace_bytes, &pa, &generic, &fp8, &paged);
+  if (st != MLA_OK || B == 0) return st;
+  st = prepare_combine(seq_lens, max_len, B, H, d_c, num_splits, workspace, workspace_bytes, o_latent, lse, &ca);
+  if (st != MLA_OK) return st;
+  st = launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_combine(ca, (hipStream_t)stream));
+}
+
+int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out, int B, int H, int d_h, int d_c,
+               void* stream) {
+  if (B < 0 || H < 1 || d_h < 1 || d_c < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(w_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!o_latent || !W_UV || !out) return MLA_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (w_dtype == MLA_F32) return hip_status(mla::launch_uv_f32w(o_latent, (const float*)W_UV, out, B, H, d_h, d_c, s));
+  if (w_dtype == MLA_BF16) {
+    if (d_h == 128 && d_c == 512 && aligned16(o_latent) && aligned16(W_UV))
+      return hip_status(mla::launch_uv_bf16(o_latent, W_UV, out, B, H, s));
+    return hip_status(mla::launch_uv_bf16w_generic(o_latent, W_UV, out, B, H, d_h, d_c, s));
+  }
+  return MLA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+"""Python binding of the C ABI (include/mla.h) over torch device tensors.
+
+Argument marshalling only: each function passes device pointers, sizes and the current HIP stream
+to the function of the same name in libmla_amd.so.  torch provides device memory and streams;
+every step of the decode runs in the library's HIP kernels.  There is no fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import CacheDesc, MLA_BF16, MLA_F32, MLA_FP8_E4M3, check
+
+_FP8_TYPES = {torch.uint8}
+if hasattr(torch, "float8_e4m3fn"):
+    _FP8_TYPES.add(torch.float8_e4m3fn)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype in _FP8_TYPES:
+        return MLA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+
+
+def _stream(stream, t: torch.Tensor) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return int(s.cuda_stream)
+
+
+class Cache:
+    """Latent + rope-key cache of one layer, as the mla_cache_desc of include/mla.h.
+
+    Holds references to the tensors so they outlive the descriptor.
+    """
+
+    def __init__(self, latent, rope, scale=None, block_table=None, page_size=0):
+        _dev(latent, rope, scale, block_table)
+        if latent.dim() != 3 or rope.dim() != 3:
+            raise ValueError("latent and rope are [B or pages, tokens, width] views")
+        if latent.stride(2) != 1 or rope.stride(2) != 1:
+            raise ValueError("latent and rope rows must be contiguous")
+        self.latent, self.rope, self.scale, self.block_table = latent, rope, scale, block_table
+        d = CacheDesc()
+        d.latent = latent.data_ptr()
+        d.rope = rope.data_ptr()
+        d.latent_scale = scale.data_ptr() if scale is not None else None
+        d.block_table = block_table.data_ptr() if block_table is not None else None
+        d.latent_dtype = dtype_code(latent)
+        d.rope_dtype = dtype_code(rope)
+        d.latent_stride_b, d.latent_stride_tok = latent.stride(0), latent.stride(1)
+        d.rope_stride_b, d.rope_stride_tok = rope.stride(0), rope.stride(1)
+        if scale is not None:
+            if scale.dtype != torch.float32 or scale.stride(-1) != 1:
+                raise ValueError("scale is a float32 [B or pages, tokens] tensor with unit token stride")
+            d.scale_stride_b = scale.stride(0)
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or not block_table.is_contiguous():
+                raise ValueError("block_table is a contiguous int32 [B, max_pages] tensor")
+            d.page_size = int(page_size)
+            d.max_pages = block_table.shape[1]
+        self.desc = d
+
+    @classmethod
+    def split(cls, latent, rope, scale=None):
+        return cls(latent, rope, scale)
+
+    @classmethod
+    def packed(cls, kv, d_c: int):
+        """kv [B, N, d_c + d_R]: latent in columns [0, d_c), rope key after."""
+        return cls(kv[..., :d_c], kv[..., d_c:])
+
+    @classmethod
+    def paged(cls, pool, block_table, d_c: int):
+        """pool [pages, page_size, d_c + d_R]; block_table [B, max_pages] int32."""
+        return cls(pool[..., :d_c], pool[..., d_c:], None, block_table, pool.shape[1])
+
+
+def mla_absorb_q(q_C: torch.Tensor, W_UK: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """q'[b,h] = W_UK[h]^T q_C[b,h].  q_C [B,H,d_h], W_UK [H,d_h,d_c]; out [B,H,d_c] (same dtype)."""
+    _dev(q_C, W_UK, out)
+    B, H, d_h = q_C.shape
+    d_c = W_UK.shape[2]
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=q_C.dtype, device=q_C.device)
+    if not (q_C.is_contiguous() and W_UK.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q_C, W_UK and out must be contiguous")
+    check("mla_absorb_q", _lib.lib().mla_absorb_q(q_C.data_ptr(), W_UK.data_ptr(), out.data_ptr(), dtype_code(q_C),
+                                                  dtype_code(out), B, H, d_h, d_c, _stream(stream, q_C)))
+    return out
+
+
+def mla_decode_workspace_bytes(B: int, H: int, d_c: int, max_len: int, num_splits: int = 0) -> int:
+    return int(_lib.lib().mla_decode_workspace_bytes(B, H, d_c, max_len, num_splits))
+
+
+def mla_decode_auto_splits(B: int, H: int, max_len: int) -> int:
+    return int(_lib.lib().mla_decode_auto_splits(B, H, max_len))
+
+
+def mla_decode_attn(q_abs: torch.Tensor, q_R: torch.Tensor, cache: Cache, seq_lens: torch.Tensor, max_len: int,
+                    scale: Optional[float] = None, d_h: Optional[int] = None, num_splits: int = 0,
+                    workspace: Optional[torch.Tensor] = None, o_latent: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """Scores against the cached latents + rope keys, softmax over j < seq_lens[b], latent sum.
+
+    Returns (o_latent [B,H,d_c] float32, lse [B,H] float32 or None).  ``scale`` defaults to
+    1/sqrt(d_h + d_R) (``d_h`` then required).
+    """
+    _dev(q_abs, q_R, seq_lens, workspace, o_latent, lse)
+    B, H, d_c = q_abs.shape
+    d_R = q_R.shape[2]
+    if scale is None:
+        if d_h is None:
+            raise ValueError("pass scale or d_h")
+        scale = 1.0 / math.sqrt(d_h + d_R)
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens is a contiguous int32 [B] tensor")
+    if not (q_abs.is_contiguous() and q_R.is_contiguous()):
+        raise ValueError("q_abs and q_R must be contiguous")
+    need = mla_decode_workspace_bytes(B, H, d_c, max_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_abs.device)
+    if o_latent is None:
+        o_latent = torch.empty((B, H, d_c), dtype=torch.float32, device=q_abs.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_abs.device)
+    st = mla_decode_attn_raw(q_abs, q_R, cache, seq_lens, max_len, scale, num_splits, workspace, o_latent, lse,
+                             stream)
+    check("mla_decode_attn", st)
+    return o_latent, lse
+
+
+def mla_decode_attn_raw(q_abs, q_R, cache: Cache, seq_lens, max_len, scale, num_splits, workspace, o_latent, lse,
+                        stream=None) -> int:
+    """Direct call; returns the status code (used by error-path tests)."""
+    B, H, d_c = q_abs.shape
+    d_R = q_R.shape[2]
+    return _lib.lib().mla_decode_attn(
+        q_abs.data_ptr(), q_R.data_ptr(), dtype_code(q_abs), ctypes.byref(cache.desc), seq_lens.data_ptr(),
+        int(max_len), B, H, d_c, d_R, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(),
+        o_latent.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream, q_abs))
+
+
+def mla_decode_partial(q_abs, q_R, cache: Cache, seq_lens, max_len: int, scale: float, workspace,
+                       num_splits: int = 0, stream=None) -> None:
+    """Partial pass of mla_decode_attn into ``workspace`` (see include/mla.h)."""
+    _dev(q_abs, q_R, seq_lens, workspace)
+    B, H, d_c = q_abs.shape
+    d_R = q_R.shape[2]
+    check("mla_decode_partial", _lib.lib().mla_decode_partial(
+        q_abs.data_ptr(), q_R.data_ptr(), dtype_code(q_abs), ctypes.byref(cache.desc), seq_lens.data_ptr(),
+        int(max_len), B, H, d_c, d_R, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(),
+        _stream(stream, q_abs)))
+
+
+def mla_decode_combine(seq_lens, max_len: int, B: int, H: int, d_c: int, workspace, o_latent, lse=None,
+                       num_splits: int = 0, stream=None) -> None:
+    """Combine pass of mla_decode_attn: workspace partials -> o_latent [B,H,d_c], lse [B,H]."""
+    _dev(seq_lens, workspace, o_latent, lse)
+    check("mla_decode_combine", _lib.lib().mla_decode_combine(
+        seq_lens.data_ptr(), int(max_len), B, H, d_c, int(num_splits), workspace.data_ptr(), workspace.numel(),
+        o_latent.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream, o_latent)))
+
+
+def mla_uv_out(o_latent: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """out[b,h] = W_UV[h] o_latent[b,h].  o_latent [B,H,d_c] float32, W_UV [H,d_h,d_c]; out [B,H,d_h] float32."""
+    _dev(o_latent, W_UV, out)
+    B, H, d_c = o_latent.shape
+    d_h = W_UV.shape[1]
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=o_latent.device)
+    if not (o_latent.is_contiguous() and W_UV.is_contiguous() and out.is_contiguous()):
+        raise ValueError("o_latent, W_UV and out must be contiguous")
+    check("mla_uv_out", _lib.lib().mla_uv_out(o_latent.data_ptr(), W_UV.data_ptr(), dtype_code(W_UV),
+                                              out.data_ptr(), B, H, d_h, d_c, _stream(stream, o_latent)))
+    return out

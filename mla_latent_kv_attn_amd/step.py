@@ -1,0 +1,32 @@
+"""One full absorbed decode step over preallocated buffers: mla_absorb_q -> mla_decode_attn ->
+mla_uv_out, all on one stream.  Buffers are allocated once (torch device memory) and reused, so a
+step issues four kernel launches and nothing else."""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import ops
+
+
+class DecodeStep:
+    def __init__(self, B: int, H: int, d_h: int, d_c: int, d_R: int, max_len: int, q_dtype: torch.dtype,
+                 device="cuda", num_splits: int = 0):
+        self.B, self.H, self.d_h, self.d_c, self.d_R, self.max_len = B, H, d_h, d_c, d_R, max_len
+        self.num_splits = num_splits
+        self.scale = 1.0 / math.sqrt(d_h + d_R)
+        self.q_abs = torch.empty((B, H, d_c), dtype=q_dtype, device=device)
+        self.o_latent = torch.empty((B, H, d_c), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((B, H, d_h), dtype=torch.float32, device=device)
+        nbytes = ops.mla_decode_workspace_bytes(B, H, d_c, max_len, num_splits)
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+    def __call__(self, q_C, q_R, W_UK, W_UV, cache: "ops.Cache", seq_lens, stream=None):
+        ops.mla_absorb_q(q_C, W_UK, out=self.q_abs, stream=stream)
+        ops.mla_decode_attn(self.q_abs, q_R, cache, seq_lens, self.max_len, scale=self.scale,
+                            num_splits=self.num_splits, workspace=self.workspace, o_latent=self.o_latent,
+                            lse=self.lse, stream=stream)
+        ops.mla_uv_out(self.o_latent, W_UV, out=self.out, stream=stream)
+        return self.out

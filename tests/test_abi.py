@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared function, and rejects
+invalid arguments with the documented status before launching anything.
+
+Pointers passed here are never dereferenced: each call fails host-side validation first (or is a
+documented no-op such as B == 0).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import pytest
+
+from mla_latent_kv_attn_amd import _lib as L
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = L.header_functions()
+    assert {"mla_absorb_q", "mla_decode_attn", "mla_uv_out", "mla_decode_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mla_version() == 10000
+    assert lib.mla_last_hip_error() == 0
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.mla_status_string(code).decode()
+        assert s.startswith("MLA_")
+    assert "unknown" in lib.mla_status_string(99).decode()
+
+
+def test_absorb_validation(lib):
+    f = lib.mla_absorb_q
+    assert f(FAKE, FAKE, FAKE, L.MLA_BF16, L.MLA_BF16, -1, 128, 128, 512, None) == L.MLA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, L.MLA_BF16, L.MLA_BF16, 1, 0, 128, 512, None) == L.MLA_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 9, L.MLA_BF16, 1, 128, 128, 512, None) == L.MLA_ERR_DTYPE
+    assert f(None, None, None, L.MLA_BF16, L.MLA_BF16, 0, 128, 128, 512, None) == L.MLA_OK   # no-op
+    assert f(None, FAKE, FAKE, L.MLA_BF16, L.MLA_BF16, 1, 128, 128, 512, None) == L.MLA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, L.MLA_BF16, L.MLA_BF16, 1, 128, 64, 512, None) == L.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, L.MLA_F32, L.MLA_BF16, 1, 128, 128, 512, None) == L.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, L.MLA_F32, L.MLA_F32, 1, 4, 16, 8192, None) == L.MLA_ERR_UNSUPPORTED
+    assert f(FAKE + 2, FAKE, FAKE, L.MLA_BF16, L.MLA_BF16, 1, 128, 128, 512, None) == L.MLA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula(lib):
+    ws = lib.mla_decode_workspace_bytes
+    assert ws(0, 128, 512, 4096, 0) == 0 and ws(1, 128, 512, -1, 0) == 0 and ws(1, 128, 512, 64, -2) == 0
+    for B, H, d_c, N, S in [(1, 128, 512, 4096, 0), (64, 128, 512, 8192, 0), (3, 4, 32, 64, 7), (16, 64, 512, 100, 1)]:
+        W = S if S else lib.mla_decode_auto_splits(B, H, N)
+        slots = W + B - 1
+        acc = (slots * H * d_c * 4 + 255) // 256 * 256
+        ml = (slots * H * 2 * 4 + 255) // 256 * 256
+        assert ws(B, H, d_c, N, S) == acc + ml
+    # the auto choice: about four 32-token tiles per workgroup, at most 256 workgroups
+    assert lib.mla_decode_auto_splits(1, 128, 4096) == 32
+    assert lib.mla_decode_auto_splits(64, 128, 8192) == 256
+    assert lib.mla_decode_auto_splits(1, 128, 1) == 1
+
+
+def _desc(latent_dtype=L.MLA_BF16, rope_dtype=L.MLA_BF16, scale=None, bt=None, page=0, max_pages=0,
+          latent=FAKE, st_tok=576, st_b=576 * 4096, rope_st=576):
+    d = L.CacheDesc()
+    d.latent, d.rope = latent, FAKE + 1024
+    d.latent_scale, d.block_table = scale, bt
+    d.latent_dtype, d.rope_dtype = latent_dtype, rope_dtype
+    d.latent_stride_b, d.latent_stride_tok = st_b, st_tok
+    d.rope_stride_b, d.rope_stride_tok = st_b, rope_st
+    d.scale_stride_b = 4096
+    d.page_size, d.max_pages = page, max_pages
+    return d
+
+
+def _attn(lib, desc, B=1, H=128, d_c=512, d_R=64, q_dtype=L.MLA_BF16, max_len=4096, scale=1 / math.sqrt(192),
+          splits=0, ws=FAKE, ws_bytes=1 << 40, q=FAKE, lens=FAKE, out=FAKE):
+    return lib.mla_decode_attn(q, FAKE, q_dtype, ctypes.byref(desc) if desc is not None else None, lens, max_len, B,
+                               H, d_c, d_R, scale, splits, ws, ws_bytes, out, None, None)
+
+
+def test_decode_attn_validation(lib):
+    d = _desc()
+    assert _attn(lib, d, B=-1) == L.MLA_ERR_SHAPE
+    assert _attn(lib, d, d_c=6) == L.MLA_ERR_SHAPE
+    assert _attn(lib, d, max_len=-5) == L.MLA_ERR_SHAPE
+    assert _attn(lib, d, scale=float("nan")) == L.MLA_ERR_SHAPE
+    assert _attn(lib, d, B=3000) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, None) == L.MLA_ERR_NULL
+    assert _attn(lib, d, q_dtype=7) == L.MLA_ERR_DTYPE
+    assert _attn(lib, _desc(latent_dtype=5)) == L.MLA_ERR_DTYPE
+    assert _attn(lib, d, B=0) == L.MLA_OK                                # no-op
+    assert _attn(lib, d, q=None) == L.MLA_ERR_NULL
+    assert _attn(lib, d, lens=None) == L.MLA_ERR_NULL
+    assert _attn(lib, d, ws=None) == L.MLA_ERR_WORKSPACE
+    need = lib.mla_decode_workspace_bytes(1, 128, 512, 4096, 0)
+    assert _attn(lib, d, ws_bytes=need - 1) == L.MLA_ERR_WORKSPACE
+    assert _attn(lib, d, d_c=256) == L.MLA_ERR_UNSUPPORTED               # bf16 path is d_c = 512 only
+    assert _attn(lib, d, H=96) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, _desc(latent=FAKE + 2)) == L.MLA_ERR_UNSUPPORTED   # misaligned rows
+    assert _attn(lib, _desc(st_tok=577)) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, _desc(latent_dtype=L.MLA_FP8_E4M3)) == L.MLA_ERR_NULL   # fp8 needs scales
+    assert _attn(lib, _desc(latent_dtype=L.MLA_F32, rope_dtype=L.MLA_F32)) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, _desc(bt=FAKE, page=48, max_pages=100)) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, _desc(bt=FAKE, page=64, max_pages=10)) == L.MLA_ERR_SHAPE   # 640 < max_len
+    assert _attn(lib, _desc(bt=FAKE, page=0, max_pages=10)) == L.MLA_ERR_SHAPE
+    assert _attn(lib, _desc(latent_dtype=L.MLA_F32, rope_dtype=L.MLA_F32), q_dtype=L.MLA_F32, d_c=2048) == \
+        L.MLA_ERR_UNSUPPORTED
+
+
+def test_uv_out_validation(lib):
+    f = lib.mla_uv_out
+    assert f(FAKE, FAKE, L.MLA_BF16, FAKE, -1, 128, 128, 512, None) == L.MLA_ERR_SHAPE
+    assert f(FAKE, FAKE, 5, FAKE, 1, 128, 128, 512, None) == L.MLA_ERR_DTYPE
+    assert f(None, FAKE, L.MLA_BF16, FAKE, 1, 128, 128, 512, None) == L.MLA_ERR_NULL
+    assert f(None, None, L.MLA_BF16, None, 0, 128, 128, 512, None) == L.MLA_OK
+    assert f(FAKE, FAKE, L.MLA_FP8_E4M3, FAKE, 1, 128, 128, 512, None) == L.MLA_ERR_UNSUPPORTED
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(L.MlaLibraryError):
+        L.lib()
