@@ -146,7 +146,7 @@ int mla_decode_auto_splits(int B, int H, int max_len);
  *   cache     host pointer to the descriptor (read during the call only)
  *   seq_lens  [B] int32 device: tokens cached per sequence, 0 <= len <= max_len
  *   max_len   host: an upper bound on every seq_lens[b]
- *   scale     softmax scale, normally 1/sqrt(d_h + d_R)
+ *   scale     softmax scale, positive and finite, normally 1/sqrt(d_h + d_R)
  *   workspace device buffer of at least mla_decode_workspace_bytes(...) bytes,
  *             any contents; overwritten
  *   o_latent  [B, H, d_c] float32 (written): sum_j a_j c_j

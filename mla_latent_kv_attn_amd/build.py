@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -40,18 +41,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the MLA library needs ROCm's hipcc to build")
 
 
+# Kernels whose DMA pipeline counts outstanding vector-memory operations (s_waitcnt vmcnt): a
+# spill to scratch memory inside them would add scratch loads/stores to that count, so they must
+# use no scratch (SGPR spills into VGPR lanes are fine).
+NO_SCRATCH_KERNELS = ("k_partial_mfma",)
+
+
+def _check_spills(src: str, remarks: str) -> None:
+    """Parse -Rpass-analysis=kernel-resource-usage remarks; fail if a guarded kernel uses scratch."""
+    current = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            current = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and current and any(k in current for k in NO_SCRATCH_KERNELS) and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: kernel {current} uses {m.group(1)} bytes/lane of scratch; "
+                               "the tile pipeline requires a register allocation without spills to memory")
+
+
 def _compile(src: str, save_temps: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
+    text = r.stdout + r.stderr
+    out = "\n".join(l for l in text.splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and "remark:" not in l
+                    and l.strip() and not l.lstrip().startswith(("|", "^")))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{out}")
-    if out.strip():
-        print(out, file=sys.stderr)
+    _check_spills(src, text)
     return obj
 
 

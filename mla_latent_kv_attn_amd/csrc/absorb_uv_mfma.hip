@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* __restrict_
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int b = b0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (b < B) orow[(int64_t)b * H * 512 + 32 * cb] = (uint16_t)f32_to_bf16_bits(acc[v]);
+      if (b < B) orow[(int64_t)b * H * 512 + 32 * cb] = (uint16_t)(pack_bf16x2(acc[v], 0.f) & 0xffffu);
     }
   }
 }
@@ -80,14 +80,12 @@ hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, in
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, u32x4& hi, u32x4& lo) {
   const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  uint32_t hb[8], lb[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    hb[j] = f32_to_bf16_bits(xs[j]);
-    lb[j] = f32_to_bf16_bits(xs[j] - bf16_bits_to_f32(hb[j]));
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h2 = pack_bf16x2(xs[2 * j], xs[2 * j + 1]);
+    hi[j] = h2;
+    lo[j] = pack_bf16x2(xs[2 * j] - __uint_as_float(h2 << 16), xs[2 * j + 1] - __uint_as_float(h2 & 0xffff0000u));
   }
-  hi = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-  lo = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
 }
 
 __global__ __launch_bounds__(128) void k_uv_bf16(const float* __restrict__ o_lat, const uint16_t* __restrict__ w,

@@ -29,6 +29,8 @@
 //    the probabilities before the value MFMA, so the MFMA operands are the exact stored codes.
 //  * Rows past a sequence's length in its last tile are loaded from the last valid row (finite
 //    data) and masked to probability 0, so padding contents (even NaN) never reach the result.
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -36,7 +38,8 @@ namespace mla {
 namespace {
 
 constexpr int kNst = 3;           // LDS ring stages
-constexpr int kLatStride = 1056;  // bytes per LDS block of 1 KiB (+32 B pad: 8 dwords mod 64 banks)
+constexpr int kLatStride = 1056;
+constexpr int kPbStride = 80;     // bytes per head row of the probability exchange buffer (64 + pad)  // bytes per LDS block of 1 KiB (+32 B pad: 8 dwords mod 64 banks)
 
 template <bool FP8>
 struct Layout {
@@ -76,17 +79,13 @@ __device__ __forceinline__ void lds_dma4(const void* gbase, uint32_t voff, uint3
                "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-// 8 E4M3 codes -> 8 bf16 (exact: every E4M3 value is a bf16 value)
+// 8 E4M3 codes -> 8 bf16 (exact: every E4M3 value is a bf16 value); v_cvt_scalef32_pk_bf16_fp8
+// with scale 1 converts two codes into one packed bf16 pair
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 v) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], true);
-  // exact values: the bf16 bits are the high halves of the fp32 bits
-  return u32x4{__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u),
-               __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u),
-               __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u),
-               __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u)};
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true))};
 }
 
 // uniform 32-bit load through the scalar data cache (s_load): keeps block-table lookups off the
@@ -99,6 +98,8 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* p) {
       (const __attribute__((address_space(4))) int32_t*)(((uint64_t)hi << 32) | lo);
   return *q;
 }
+
+constexpr int lgkmcnt_imm0() { return 15 | (3 << 14) | (7 << 4); }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -118,6 +119,13 @@ void k_partial_mfma(PartialArgs a) {
   __shared__ int P[kMaxB + 1];
   __shared__ int L[kMaxB];
   __shared__ __attribute__((aligned(16))) uint8_t qrs[NWAVE * 32 * 128];  // q_R of each wave's heads
+  // fp8 variant: the last (32 - QREG) latent k-steps of Qhat live in LDS (its tiles are half the
+  // size of bf16 tiles, which leaves room), freeing registers for the fp8 widening
+  constexpr int QREG = FP8 ? 24 : 32;
+  __shared__ __attribute__((aligned(16))) uint8_t qls[FP8 ? NWAVE * (32 - QREG) * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[NWAVE * 32 * kPbStride];  // bf16 probabilities
+  __shared__ float alpha_s[NWAVE * 32];   // rescale factor of each head (valid when its flag is set)
+  __shared__ int flags_s[NWAVE];          // 1 if the wave's heads were rescaled this tile
 
   build_tile_prefix(a.seq_lens, a.B, P, L);
   const int NT = P[a.B];
@@ -165,22 +173,23 @@ void k_partial_mfma(PartialArgs a) {
       srow0 = (int64_t)b * a.scale_sb;
       tslot0 = tok0;
     }
+    // byte address of row 0 of the tile; rows advance by the token stride (a 32-bit offset)
+    const uint8_t* lbase = latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * (FP8 ? 1 : 2);
+    const uint32_t lstride = (uint32_t)a.lat_st * (FP8 ? 1u : 2u);
     if (!FP8) {
 #pragma unroll
       for (int i = 0; i < 32 / NWAVE; ++i) {
         const int r = wave + NWAVE * i;
-        const int tok = tslot0 + min(r, last);
-        const uint8_t* gb = latent + (lrow0 + (int64_t)tok * a.lat_st) * 2;
-        lds_dma16(gb, ((r >> 3) & 1) ? vx1 : vx0, st + r * kLatStride);
+        const uint32_t roff = (uint32_t)min(r, last) * lstride;
+        lds_dma16(lbase, (((r >> 3) & 1) ? vx1 : vx0) + roff, st + r * kLatStride);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 16 / NWAVE; ++i) {
         const int pr = wave + NWAVE * i;       // row pair
-        const int tok = tslot0 + min(2 * pr, last);
-        const uint8_t* gb = latent + (lrow0 + (int64_t)tok * a.lat_st);
-        const uint32_t second = (2 * pr + 1 <= last) ? (uint32_t)a.lat_st : 0u;  // row 2pr+1 (or 2pr again)
-        lds_dma16(gb, (lane >> 5) ? second + vf1 : vf0, st + pr * kLatStride);
+        const uint32_t r0 = (uint32_t)min(2 * pr, last) * lstride;
+        const uint32_t r1 = (uint32_t)min(2 * pr + 1, last) * lstride;
+        lds_dma16(lbase, (lane >> 5) ? r1 + vf1 : r0 + vf0, st + pr * kLatStride);
       }
 #pragma unroll
       for (int i = 0; i < 4 / NWAVE; ++i) {
@@ -206,8 +215,9 @@ void k_partial_mfma(PartialArgs a) {
   };
 
   // ---------------------------------------------------------------- per-lane constants
+  constexpr int CPW = 16 / NWAVE;           // 32-column blocks of the latent owned by each wave
   const int hf = lane >> 5;                 // lane half
-  const int h = wave * 32 + (lane & 31);    // this lane's head
+  const int h = wave * 32 + (lane & 31);    // this lane's head in the score phase
   const int srow = pi_row(lane & 31);       // score-operand row (token within tile)
   const int G = lane >> 4;                  // 16-lane group
   // LDS read bases (bytes inside a stage); every k-step / column block adds an immediate offset
@@ -217,6 +227,7 @@ void k_partial_mfma(PartialArgs a) {
   //  value, bf16: rows 16ks + vrow0 (+4), chunk 4cb + 2(G&1) + ((lane&3)>>1 ^ swz), +8 (lane&1)
   //                                                                           -> base + 16896 ks + 64 cb
   //  value, fp8:  rows 16ks + vrow0, chunk 2cb + ((G&1) ^ (vrow0&1)), +8 (lane&1) -> base + 8448 ks + 32 cb
+  //  probabilities (pbuf): head row of 80 bytes, tokens 16ks + 8hf .. +7     -> base + 32 ks (+ 2560 hb)
   const int vrow0 = FP8 ? 8 * (G >> 1) + ((lane & 15) >> 1) : 8 * (G >> 1) + ((lane & 15) >> 2);
   int sc_base, sc_base_odd, val_base;
   if (!FP8) {
@@ -231,6 +242,7 @@ void k_partial_mfma(PartialArgs a) {
   }
   const int rope_base = LY::kRopeOff + 16 * (hf * 32 + srow);
   const int qr_base = 16 * (hf * 32 + (lane & 31));
+  const int pb_base = (lane & 31) * kPbStride + 16 * hf;
 
   issue(0);
   if (ntiles > 1) issue(1);
@@ -244,11 +256,16 @@ void k_partial_mfma(PartialArgs a) {
     const int it_end = min(ntiles, P[b + 1] - t_begin);
     const int len_b = L[b];
 
-    u32x4 qf[32];
+    u32x4 qf[QREG];
     {
       const uint16_t* qa = (const uint16_t*)a.q_abs + ((int64_t)b * H + h) * 512 + 8 * hf;
 #pragma unroll
-      for (int s = 0; s < 32; ++s) qf[s] = *(const u32x4*)(qa + 16 * s);
+      for (int s = 0; s < QREG; ++s) qf[s] = *(const u32x4*)(qa + 16 * s);
+      // k-steps QREG..31 -> this wave's LDS block, slot (2 (s - QREG) + hf) * 32 + head
+#pragma unroll
+      for (int s = QREG; s < 32; ++s)
+        *(u32x4*)(qls + wave * (32 - QREG) * 1024 + 16 * ((2 * (s - QREG) + hf) * 32 + (lane & 31))) =
+            *(const u32x4*)(qa + 16 * s);
       // q_R of head h -> this wave's LDS block, chunk-major (slot 32c + head)
       const uint16_t* qr = (const uint16_t*)a.q_R + ((int64_t)b * H + h) * 64;
 #pragma unroll
@@ -261,10 +278,11 @@ void k_partial_mfma(PartialArgs a) {
     // flight), so that no wait on them is left inside the tile loop, where any vmcnt wait would
     // also drain the tile DMA pipeline.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // acc[hb * CPW + j]: O^T rows (latent columns) 32 * (wave * CPW + j) .. +31, heads 32 hb .. +31
     f32x16 acc[16];
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;   // of head h (score phase)
 
     for (; it < it_end; ++it) {
       if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
@@ -275,27 +293,38 @@ void k_partial_mfma(PartialArgs a) {
       const int nvalid = min(kTile, len_b - (t_begin + it - P[b]) * kTile);
       const uint8_t* st = smem + (it % kNst) * LY::kStage;
 
-      // ---- score block: S^T[token rows][heads], 32 latent k-steps + 4 rope k-steps
+      // ---- score block of this wave's 32 heads: S^T[token rows][heads]
       f32x16 S = {}, S2 = {};
-      auto lat_op = [&](int s) -> u32x4 {
-        if (!FP8) return *(const u32x4*)(st + sc_base + 32 * s);
-        return fp8x8_to_bf16x8(*(const u32x2*)(st + ((s & 1) ? sc_base_odd : sc_base) + 16 * s));
+      // latent score operand: bf16 rows read as 16 bytes; fp8 rows read as 8 raw bytes and widened
+      // to bf16 just before the MFMA that consumes them (keeps prefetched operands small)
+      using LatRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
+      auto lat_op = [&](int s) -> LatRaw {
+        if constexpr (!FP8) return *(const u32x4*)(st + sc_base + 32 * s);
+        else return *(const u32x2*)(st + ((s & 1) ? sc_base_odd : sc_base) + 16 * s);
+      };
+      auto widen = [&](const LatRaw& r) -> u32x4 {
+        if constexpr (!FP8) return r;
+        else return fp8x8_to_bf16x8(r);
       };
       auto rope_op = [&](int q) -> u32x4 { return *(const u32x4*)(st + rope_base + 1024 * q); };
-      u32x4 a0 = lat_op(0), a1 = lat_op(1);
+      auto q_lds = [&](int s) -> u32x4 {
+        return *(const u32x4*)(qls + wave * (32 - QREG) * 1024 + qr_base + 1024 * (s - QREG));
+      };
+      LatRaw a0 = lat_op(0), a1 = lat_op(1);
 #pragma unroll
       for (int s = 0; s < 32; s += 2) {
-        u32x4 n0, n1;
+        LatRaw n0 = a0, n1 = a1;
         if (s + 2 < 32) {
           n0 = lat_op(s + 2);
           n1 = lat_op(s + 3);
-        } else {
-          n0 = rope_op(0);
-          n1 = rope_op(1);
         }
         asm volatile("" ::: "memory");
-        S = mfma32x32x16(a0, qf[s], S);
-        S = mfma32x32x16(a1, qf[s + 1], S);
+        // two accumulators: consecutive MFMAs are independent (a dependent 32x32x16 chain issues
+        // at roughly 60% of the independent rate)
+        const u32x4 q0 = (s < QREG) ? qf[s < QREG ? s : 0] : q_lds(s);
+        const u32x4 q1 = (s + 1 < QREG) ? qf[s + 1 < QREG ? s + 1 : 0] : q_lds(s + 1);
+        S = mfma32x32x16(widen(a0), q0, S);
+        S2 = mfma32x32x16(widen(a1), q1, S2);
         a0 = n0;
         a1 = n1;
       }
@@ -306,112 +335,152 @@ void k_partial_mfma(PartialArgs a) {
         const u32x4 b1 = *(const u32x4*)(qrow + 1024);
         const u32x4 b2 = *(const u32x4*)(qrow + 2048);
         const u32x4 b3 = *(const u32x4*)(qrow + 3072);
-        const u32x4 n2 = rope_op(2);
-        const u32x4 n3 = rope_op(3);
+        const u32x4 r0 = rope_op(0), r1 = rope_op(1), r2 = rope_op(2), r3 = rope_op(3);
         if (FP8) {
-          S2 = mfma32x32x16(a0, b0, S2);
-          S2 = mfma32x32x16(a1, b1, S2);
-          S2 = mfma32x32x16(n2, b2, S2);
-          S2 = mfma32x32x16(n3, b3, S2);
+          S += S2;  // latent part (scaled per token in the softmax); rope part accumulates in S2
+          S2 = f32x16{};
+          S2 = mfma32x32x16(r0, b0, S2);
+          S2 = mfma32x32x16(r1, b1, S2);
+          S2 = mfma32x32x16(r2, b2, S2);
+          S2 = mfma32x32x16(r3, b3, S2);
         } else {
-          S = mfma32x32x16(a0, b0, S);
-          S = mfma32x32x16(a1, b1, S);
-          S = mfma32x32x16(n2, b2, S);
-          S = mfma32x32x16(n3, b3, S);
+          S = mfma32x32x16(r0, b0, S);
+          S2 = mfma32x32x16(r1, b1, S2);
+          S = mfma32x32x16(r2, b2, S);
+          S2 = mfma32x32x16(r3, b3, S2);
         }
       }
-
       // keep the score block in VGPRs (the softmax works on it with VALU ops)
-      asm volatile("" : "+v"(S));
-      if (FP8) asm volatile("" : "+v"(S2));
+      asm volatile("" : "+v"(S), "+v"(S2));
 
       // ---- online softmax (log2 units); lane holds 16 tokens of head h
+      //      raw score x_j (unscaled); p_j = 2^(x_j * scale * log2e - m)
+      //      element i of the lane holds token 16 (i >> 3) + 8 hf + (i & 7) of the tile
       float mx = -INFINITY;
+      const uint8_t* scl = st + LY::kScaleOff + 32 * hf;  // fp8 per-token scales of this lane's tokens
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int tl = 16 * (i >> 3) + 8 * hf + (i & 7);
         float x = S[i];
-        if (FP8) x = x * *(const float*)(st + LY::kScaleOff + 4 * tl) + S2[i];
-        S[i] = (tl < nvalid) ? x * a.sl2 : -INFINITY;
-        mx = fmaxf(mx, S[i]);
+        if (FP8) x *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
+        S[i] = x + S2[i];  // bf16: odd k-steps; fp8: rope part
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (nvalid < kTile) {  // ragged last tile of a sequence: mask rows past its length
+        const int nv = nvalid - 8 * hf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i >> 3) + (i & 7) >= nv) S[i] = -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.sl2;
       const bool need = mx > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+      if (any) {
         const float m_new = need ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
-        // in-place AGPR rescale, one register at a time (keeps the accumulator resident in AGPRs)
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float x = acc[cb][v];
-            float t;
-            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                         : "+a"(x), "=&v"(t) : "v"(alpha));
-            acc[cb][v] = x;
-          }
-        }
+        if (lane < 32) alpha_s[h] = alpha;
       }
+      if (lane == 0) flags_s[wave] = any ? 1 : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        S[i] = __builtin_amdgcn_exp2f(S[i] - m_run);
+        S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], a.sl2, -m_run));
         l_run += S[i];
       }
       if (FP8) {
+        // re-read the per-token scales here instead of keeping 16 of them live across the softmax
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tl = 16 * (i >> 3) + 8 * hf + (i & 7);
-          S[i] *= *(const float*)(st + LY::kScaleOff + 4 * tl);
+        for (int i = 0; i < 16; ++i) S[i] *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
+      }
+      {
+        const u32x4 pb0 = {pack_bf16x2(S[0], S[1]), pack_bf16x2(S[2], S[3]), pack_bf16x2(S[4], S[5]),
+                           pack_bf16x2(S[6], S[7])};
+        const u32x4 pb1 = {pack_bf16x2(S[8], S[9]), pack_bf16x2(S[10], S[11]), pack_bf16x2(S[12], S[13]),
+                           pack_bf16x2(S[14], S[15])};
+        uint8_t* pw = pbuf + wave * 32 * kPbStride + pb_base;
+        *(u32x4*)(pw) = pb0;
+        *(u32x4*)(pw + 32) = pb1;
+      }
+      // publish probabilities, rescale factors and flags of every wave's heads
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
+      lds_barrier();
+
+      // ---- value block: this wave's latent columns for all heads of the workgroup
+      //      acc[hb][j] (O^T, columns 32 (wave*CPW + j) .., heads 32 hb ..) += C^T . P
+#pragma unroll
+      for (int hb = 0; hb < NWAVE; ++hb) {
+        if (flags_s[hb]) {
+          const float al = alpha_s[hb * 32 + (lane & 31)];
+          // in-place AGPR rescale, one register at a time (keeps the accumulator in AGPRs)
+#pragma unroll
+          for (int j = 0; j < CPW; ++j) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              float x = acc[hb * CPW + j][v];
+              float t;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(x), "=&v"(t) : "v"(al));
+              acc[hb * CPW + j][v] = x;
+            }
+          }
         }
       }
-      const u32x4 pb0 = {pack_bf16x2(S[0], S[1]), pack_bf16x2(S[2], S[3]), pack_bf16x2(S[4], S[5]),
-                         pack_bf16x2(S[6], S[7])};
-      const u32x4 pb1 = {pack_bf16x2(S[8], S[9]), pack_bf16x2(S[10], S[11]), pack_bf16x2(S[12], S[13]),
-                         pack_bf16x2(S[14], S[15])};
-
-      // ---- value block: acc[cb] (O^T rows 32cb..32cb+31 of head h) += C^T . P
-      auto val_op = [&](int cb, int ks) -> u32x4 {
-        if (!FP8) {
+      auto val_op = [&](int cb, int ks) -> LatRaw {
+        if constexpr (!FP8) {
           const uint8_t* p0 = st + val_base + 16 * kLatStride * ks + 64 * cb;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLatStride));
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
           return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        } else {
+          const uint8_t* p0 = st + val_base + 8 * kLatStride * ks + 32 * cb;
+          const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(p0));
+          return __builtin_bit_cast(u32x2, v);
         }
-        const uint8_t* p0 = st + val_base + 8 * kLatStride * ks + 32 * cb;
-        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(p0));
-        return fp8x8_to_bf16x8(__builtin_bit_cast(u32x2, v));
       };
-      u32x4 v0 = val_op(0, 0), v1 = val_op(0, 1);
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        u32x4 w0 = v0, w1 = v1;
-        if (cb + 1 < 16) { w0 = val_op(cb + 1, 0); w1 = val_op(cb + 1, 1); }
-        asm volatile("" ::: "memory");
-        acc[cb] = mfma32x32x16(v0, pb0, acc[cb]);
-        acc[cb] = mfma32x32x16(v1, pb1, acc[cb]);
-        asm volatile("" : "+a"(acc[cb]));  // the output accumulator lives in AGPRs
-        v0 = w0; v1 = w1;
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 pbv[NWAVE];
+#pragma unroll
+        for (int hb = 0; hb < NWAVE; ++hb) pbv[hb] = *(const u32x4*)(pbuf + hb * 32 * kPbStride + pb_base + 32 * ks);
+#pragma unroll
+        for (int j0 = 0; j0 < CPW; j0 += 2) {
+          const u32x4 av0 = widen(val_op(wave * CPW + j0, ks));
+          const u32x4 av1 = widen(val_op(wave * CPW + j0 + 1, ks));
+#pragma unroll
+          for (int hb = 0; hb < NWAVE; ++hb) {
+            acc[hb * CPW + j0] = mfma32x32x16(av0, pbv[hb], acc[hb * CPW + j0]);
+            acc[hb * CPW + j0 + 1] = mfma32x32x16(av1, pbv[hb], acc[hb * CPW + j0 + 1]);
+          }
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
     }
 
     // ------------------------------------------------------------ segment partial -> slot w + b
     {
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-      const int64_t o = (int64_t)(w + b) * H + h;
-      float* dst = a.ws_acc + o * 512 + 4 * hf;
+      const int64_t slot = (int64_t)(w + b) * H;
+      // opaque copy of the lane id: keeps these addresses from being hoisted out of the segment
+      // loop (where they would occupy registers for the whole tile loop)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
+      for (int hb = 0; hb < NWAVE; ++hb) {
+        float* dst = a.ws_acc + (slot + hb * 32 + (ln & 31)) * 512 + 32 * wave * CPW + 4 * (ln >> 5);
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          *(f32x4*)(dst + 32 * cb + 8 * v4) =
-              f32x4{acc[cb][4 * v4], acc[cb][4 * v4 + 1], acc[cb][4 * v4 + 2], acc[cb][4 * v4 + 3]};
+        for (int j = 0; j < CPW; ++j) {
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x16& A = acc[hb * CPW + j];
+            *(f32x4*)(dst + 32 * j + 8 * v4) = f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
+          }
         }
       }
-      if (lane < 32) *(f32x2*)(a.ws_ml + o * 2) = f32x2{m_run, l_tot};
+      if (ln < 32) *(f32x2*)(a.ws_ml + (slot + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};
     }
   }
 }

@@ -97,7 +97,7 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   if (!known_dtype(q_dtype)) return MLA_ERR_DTYPE;
   if (!cache) return MLA_ERR_NULL;
   if (!known_dtype(cache->latent_dtype) || !known_dtype(cache->rope_dtype)) return MLA_ERR_DTYPE;
-  if (!isfinite(scale)) return MLA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return MLA_ERR_SHAPE;
   if (B == 0) return MLA_OK;
   if (!q_abs || !q_R || !seq_lens || !cache->latent || !cache->rope) return MLA_ERR_NULL;
   if (cache->latent_stride_tok < 1 || cache->rope_stride_tok < 1 || cache->latent_stride_b < 0 ||
