@@ -122,6 +122,9 @@ int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, i
  * Workspace (device bytes) mla_decode_attn needs for these sizes.  num_splits
  * is the number of partial-pass workgroups over the whole batch (0 = the
  * library's choice for (B, H, max_len), the same choice mla_decode_attn makes).
+ * With W workgroups the workspace holds (W + B - 1) partial slots of H x d_c
+ * float sums and H (max, sum) pairs, then B + 1 int32 tile prefix sums; each of
+ * the three regions is rounded up to a multiple of 256 bytes.
  * Returns 0 for invalid sizes.
  */
 size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits);
@@ -172,6 +175,8 @@ int mla_decode_attn(const void* q_abs, const void* q_R, int q_dtype, const mla_c
  *     (workgroup, sequence) segment into the workspace.
  *   mla_decode_combine: merges the partials of each (b, h) into o_latent and lse (the
  *     log-sum-exp merge: M = max m_s, L = sum 2^(m_s-M) l_s, o = sum 2^(m_s-M) acc_s / L).
+ *     It reads the segment layout (tile prefix sums of seq_lens) that the partial pass left
+ *     in the workspace, so it must follow a partial pass over the same seq_lens.
  */
 int mla_decode_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
                        const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,

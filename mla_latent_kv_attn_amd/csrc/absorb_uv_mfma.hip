@@ -65,7 +65,77 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// absorb, small batch (B <= 4): a plain stream over W_UK (no reuse to exploit).  Grid (H, 4 column
+// quarters), 256 threads.  Thread t owns columns 8 (t % 16) .. +7 of its quarter and rows
+// t / 16 + 16 j (j = 0..7): eight 16-byte weight loads in flight per thread.  The 16 row groups
+// are summed through LDS.
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void k_absorb_gemv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
+                                                     uint16_t* __restrict__ out, int B, int H) {
+  constexpr int kRed = 128 + 4;
+  __shared__ __attribute__((aligned(16))) float red[16 * NB * kRed];
+  const int h = blockIdx.x, quarter = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid & 15, rg = tid >> 4;
+  const uint16_t* wp = w + ((int64_t)h * 128 + rg) * 512 + quarter * 128 + cg * 8;
+  u32x4 wv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wv[j] = *(const u32x4*)(wp + (int64_t)j * 16 * 512);
+  float qv[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qv[b][j] = b < B ? bf16_bits_to_f32(q[((int64_t)b * H + h) * 128 + rg + 16 * j]) : 0.f;
+  float acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[b][c] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const float w0 = __uint_as_float(wv[j][c2] << 16), w1 = __uint_as_float(wv[j][c2] & 0xffff0000u);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        acc[b][2 * c2] = fmaf(qv[b][j], w0, acc[b][2 * c2]);
+        acc[b][2 * c2 + 1] = fmaf(qv[b][j], w1, acc[b][2 * c2 + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float* r = &red[(rg * NB + b) * kRed + cg * 8];
+    *(float4*)r = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    *(float4*)(r + 4) = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+  }
+  __syncthreads();
+  for (int o = tid; o < NB * 128; o += 256) {
+    const int b = o >> 7, col = o & 127;
+    if (b >= B) break;
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) v += red[(g * NB + b) * kRed + col];
+    out[((int64_t)b * H + h) * 512 + quarter * 128 + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+  }
+}
+
 hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, int H, hipStream_t s) {
+  if (B <= 4) {
+    const dim3 grid(H, 4);
+    if (B == 1)
+      hipLaunchKernelGGL(k_absorb_gemv<1>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
+                         (uint16_t*)out, B, H);
+    else if (B == 2)
+      hipLaunchKernelGGL(k_absorb_gemv<2>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
+                         (uint16_t*)out, B, H);
+    else
+      hipLaunchKernelGGL(k_absorb_gemv<4>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
+                         (uint16_t*)out, B, H);
+    return hipGetLastError();
+  }
   dim3 grid(H, 2, (B + 127) / 128);
   hipLaunchKernelGGL(k_absorb_bf16, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w, (uint16_t*)out,
                      B, H);
@@ -120,7 +190,81 @@ __global__ __launch_bounds__(128) void k_uv_bf16(const float* __restrict__ o_lat
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// uv, small batch (B <= 4): a plain stream over W_UV in fp32 arithmetic.  Grid (H, 4 quarters of
+// the 128 output rows), 256 threads; wave v takes rows 32 q + 8 v .. +7 and lane l holds columns
+// 8 l .. 8 l + 7 of those rows and of o_lat.  The NB x 8 dot products are summed over the 64 lanes
+// by a halving exchange: at each step a lane keeps one half of its values and adds the partner's
+// copy of that half, so K values need K - 1 + log2(64 / K) exchanges instead of 6 K.
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat, const uint16_t* __restrict__ w,
+                                                 float* __restrict__ out, int B, int H) {
+  constexpr int K = NB * 8;                      // values per lane: index b * 8 + r
+  constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : 5;
+  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i0 = blockIdx.y * 32 + wave * 8;
+  const uint16_t* wp = w + ((int64_t)h * 128 + i0) * 512 + 8 * lane;
+  u32x4 wv[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) wv[r] = *(const u32x4*)(wp + r * 512);
+  float x[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (b < B) {
+      const float* xp = o_lat + ((int64_t)b * H + h) * 512 + 8 * lane;
+      x0 = *(const float4*)xp;
+      x1 = *(const float4*)(xp + 4);
+    }
+    x[b][0] = x0.x; x[b][1] = x0.y; x[b][2] = x0.z; x[b][3] = x0.w;
+    x[b][4] = x1.x; x[b][5] = x1.y; x[b][6] = x1.z; x[b][7] = x1.w;
+  }
+  float v[K];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        s = fmaf(x[b][2 * c2], __uint_as_float(wv[r][c2] << 16), s);
+        s = fmaf(x[b][2 * c2 + 1], __uint_as_float(wv[r][c2] & 0xffff0000u), s);
+      }
+      v[b * 8 + r] = s;
+    }
+  // halving exchange over lane bits 5, 4, ...: afterwards lane l holds value (l >> (6 - LK)) & (K - 1)
+#pragma unroll
+  for (int step = 0; step < LK; ++step) {
+    const int d = 32 >> step;
+    const int half = K >> (step + 1);
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? v[i] : v[i + half];
+      const float keep = upper ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, d, 64);
+    }
+  }
+  float t = v[0];
+#pragma unroll
+  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+  const int idx = (lane >> (6 - LK)) & (K - 1);
+  const int b = idx >> 3, r = idx & 7;
+  if ((lane & ((64 >> LK) - 1)) == 0 && b < B) out[((int64_t)b * H + h) * 128 + i0 + r] = t;
+}
+
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s) {
+  if (B <= 4) {
+    const dim3 grid(H, 4);
+    if (B == 1)
+      hipLaunchKernelGGL(k_uv_gemv<1>, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+    else if (B == 2)
+      hipLaunchKernelGGL(k_uv_gemv<2>, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+    else
+      hipLaunchKernelGGL(k_uv_gemv<4>, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+    return hipGetLastError();
+  }
   dim3 grid(H, 2, (B + 31) / 32);
   hipLaunchKernelGGL(k_uv_bf16, grid, dim3(128), 0, s, o_lat, (const uint16_t*)w, out, B, H);
   return hipGetLastError();

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
   __shared__ float qs[1024 + 256];
   __shared__ float ss[kTile];
   build_tile_prefix(a.seq_lens, a.B, P, L);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
   const int NT = P[a.B];
   const int Wp = min(a.W, NT);
   const int w = blockIdx.x;
@@ -135,56 +137,85 @@ hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
 // Combine pass: for (b, h) merge the partials of the segments of sequence b.
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) acc_s / L,
 //   lse = (M + log2 L) * ln 2       (natural log).   No segment -> o = 0, lse = -inf.
-// Grid (ceil(H/4), B), 256 threads: 64 threads per head, 4 heads per workgroup.
+// Grid (H, B), 256 threads; thread t owns columns 2t + 512 j.  The segments of sequence b are the
+// partial-pass workgroups w0..w1 whose tile ranges meet b's tiles (prefix sums from the partial pass).
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float u = __shfl_xor(v, d, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  __shared__ int P[kMaxB + 1];
-  __shared__ int L[kMaxB];
-  build_tile_prefix(a.seq_lens, a.B, P, L);
-  const int b = blockIdx.y;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (h >= a.H) return;
-  const int d_c = a.d_c;
-  const int NT = P[a.B];
-  const int tb = P[b + 1] - P[b];
-  float* out = a.o_latent + ((int64_t)b * a.H + h) * d_c;
-  if (tb == 0) {
-    for (int k = lane * 4; k < d_c; k += 256) *(float4*)(out + k) = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.lse && lane == 0) a.lse[(int64_t)b * a.H + h] = -INFINITY;
+  __shared__ float red[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d_c = a.d_c, H = a.H;
+  const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
+  float* out = a.o_latent + ((int64_t)b * H + h) * d_c;
+  if (Pb1 == Pb) {
+    for (int k = 2 * tid; k < d_c; k += 512) *(float2*)(out + k) = make_float2(0.f, 0.f);
+    if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
     return;
   }
   const int Wp = min(a.W, NT);
   // workgroup that owns tile t: ceil((t+1)*Wp/NT) - 1
-  const int w0 = (int)(((int64_t)(P[b] + 1) * Wp + NT - 1) / NT) - 1;
-  const int w1 = (int)(((int64_t)P[b + 1] * Wp + NT - 1) / NT) - 1;
+  const int w0 = (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;
+  const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
+  const int nseg = w1 - w0 + 1;
+  const float* ml = a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2;   // segment s at ml + 2 H s
+  const int64_t mstride = 2 * (int64_t)H;
+
   float M = -INFINITY;
-  for (int w = w0; w <= w1; ++w) M = fmaxf(M, a.ws_ml[((int64_t)(w + b) * a.H + h) * 2]);
-  float Lsum = 0.f;
-  for (int w = w0; w <= w1; ++w) {
-    const float* ml = a.ws_ml + ((int64_t)(w + b) * a.H + h) * 2;
-    Lsum += exp2f(ml[0] - M) * ml[1];
-  }
-  const float inv = 1.f / Lsum;
-  for (int k = lane * 4; k < d_c; k += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int w = w0; w <= w1; ++w) {
-      const int64_t o = ((int64_t)(w + b) * a.H + h);
-      const float f = exp2f(a.ws_ml[o * 2] - M);
-      const float4 v = *(const float4*)(a.ws_acc + o * d_c + k);
-      acc.x = fmaf(f, v.x, acc.x);
-      acc.y = fmaf(f, v.y, acc.y);
-      acc.z = fmaf(f, v.z, acc.z);
-      acc.w = fmaf(f, v.w, acc.w);
+  for (int s = tid; s < nseg; s += blockDim.x) M = fmaxf(M, ml[s * mstride]);
+  M = block_reduce(M, true, red);
+  float Ls = 0.f;
+  for (int s = tid; s < nseg; s += blockDim.x) Ls += exp2f(ml[s * mstride] - M) * ml[s * mstride + 1];
+  Ls = block_reduce(Ls, false, red);
+  const float inv = 1.f / Ls;
+
+  const float* acc0 = a.ws_acc + ((int64_t)(w0 + b) * H + h) * d_c;   // segment s at acc0 + H d_c s
+  const int64_t astride = (int64_t)H * d_c;
+  for (int k = 2 * tid; k < d_c; k += 512) {
+    float2 o = make_float2(0.f, 0.f);
+    int s = 0;
+    for (; s + 4 <= nseg; s += 4) {
+      float2 v[4];
+      float f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = *(const float2*)(acc0 + (s + u) * astride + k);
+        f[u] = ml[(s + u) * mstride];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = exp2f(f[u] - M);
+        o.x = fmaf(wgt, v[u].x, o.x);
+        o.y = fmaf(wgt, v[u].y, o.y);
+      }
     }
-    acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-    *(float4*)(out + k) = acc;
+    for (; s < nseg; ++s) {
+      const float2 v = *(const float2*)(acc0 + s * astride + k);
+      const float wgt = exp2f(ml[s * mstride] - M);
+      o.x = fmaf(wgt, v.x, o.x);
+      o.y = fmaf(wgt, v.y, o.y);
+    }
+    o.x *= inv;
+    o.y *= inv;
+    *(float2*)(out + k) = o;
   }
-  if (a.lse && lane == 0) a.lse[(int64_t)b * a.H + h] = (M + log2f(Lsum)) * 0.69314718055994530942f;
+  if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((a.H + 3) / 4, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

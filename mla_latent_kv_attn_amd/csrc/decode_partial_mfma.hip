@@ -128,6 +128,8 @@ void k_partial_mfma(PartialArgs a) {
   __shared__ int flags_s[NWAVE];          // 1 if the wave's heads were rescaled this tile
 
   build_tile_prefix(a.seq_lens, a.B, P, L);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
   const int NT = P[a.B];
   const int Wp = min(a.W, NT);
   const int w = blockIdx.x;

@@ -78,7 +78,7 @@ int mla_decode_auto_splits(int B, int H, int max_len) {
 size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits) {
   if (B < 1 || H < 1 || d_c < 1 || max_len < 0 || num_splits < 0) return 0;
   const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
-  return mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+  return mla::ws_total_bytes(W, B, H, d_c);
 }
 
 }  // extern "C"
@@ -110,7 +110,7 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   }
   const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
   if (W > 65535) return MLA_ERR_SHAPE;
-  const size_t need = mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+  const size_t need = mla::ws_total_bytes(W, B, H, d_c);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
 
   if (q_dtype == MLA_F32 && cache->latent_dtype == MLA_F32 && cache->rope_dtype == MLA_F32) {
@@ -156,6 +156,7 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   pa->sl2 = scale * 1.4426950408889634f;
   pa->ws_acc = (float*)workspace;
   pa->ws_ml = (float*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
+  pa->ws_prefix = (int*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H));
   return MLA_OK;
 }
 
@@ -172,7 +173,7 @@ int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c,
   if (!seq_lens || !o_latent) return MLA_ERR_NULL;
   const int W = num_splits > 0 ? num_splits : auto_splits(B, H, max_len);
   if (W > 65535) return MLA_ERR_SHAPE;
-  const size_t need = mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H);
+  const size_t need = mla::ws_total_bytes(W, B, H, d_c);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   ca->seq_lens = seq_lens;
   ca->B = B;
@@ -181,6 +182,7 @@ int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c,
   ca->W = W;
   ca->ws_acc = (const float*)workspace;
   ca->ws_ml = (const float*)((const char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
+  ca->ws_prefix = (const int*)((const char*)workspace + mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H));
   ca->o_latent = o_latent;
   ca->lse = lse;
   return MLA_OK;

@@ -36,6 +36,7 @@ struct PartialArgs {
   float sl2;                    // softmax scale * log2(e)
   float* ws_acc;                // [slots, H, d_c]
   float* ws_ml;                 // [slots, H, 2]   (m in log2 units, l)
+  int* ws_prefix;               // [B + 1] tile prefix sums (written by workgroup 0)
 };
 
 struct CombineArgs {
@@ -44,6 +45,7 @@ struct CombineArgs {
   int W;
   const float* ws_acc;
   const float* ws_ml;
+  const int* ws_prefix;         // [B + 1] tile prefix sums from the partial pass
   float* o_latent;              // [B, H, d_c]
   float* lse;                   // [B, H] or nullptr
 };
@@ -57,6 +59,10 @@ inline size_t ws_acc_bytes(int W, int B, int H, int d_c) {
 inline size_t ws_ml_bytes(int W, int B, int H) {
   size_t b = ws_slots(W, B) * (size_t)H * 2 * sizeof(float);
   return (b + 255) & ~(size_t)255;
+}
+inline size_t ws_prefix_bytes(int B) { return (((size_t)B + 1) * sizeof(int) + 255) & ~(size_t)255; }
+inline size_t ws_total_bytes(int W, int B, int H, int d_c) {
+  return ws_acc_bytes(W, B, H, d_c) + ws_ml_bytes(W, B, H) + ws_prefix_bytes(B);
 }
 
 // launchers (return the launch error; host-side validation happens in mla_abi.cpp)

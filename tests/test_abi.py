@@ -58,7 +58,8 @@ def test_workspace_size_formula(lib):
         slots = W + B - 1
         acc = (slots * H * d_c * 4 + 255) // 256 * 256
         ml = (slots * H * 2 * 4 + 255) // 256 * 256
-        assert ws(B, H, d_c, N, S) == acc + ml
+        prefix = ((B + 1) * 4 + 255) // 256 * 256
+        assert ws(B, H, d_c, N, S) == acc + ml + prefix
     # the auto choice: about four 32-token tiles per workgroup, at most 256 workgroups
     assert lib.mla_decode_auto_splits(1, 128, 4096) == 32
     assert lib.mla_decode_auto_splits(64, 128, 8192) == 256

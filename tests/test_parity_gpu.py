@@ -229,3 +229,23 @@ def test_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(step.out, eager)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 33, 129])
+def test_projections_batch_sweep(B):
+    """The two projections alone at batch sizes on both sides of the small-batch switch (B <= 4
+    streams the weights, larger batches use MFMA tiles of 128 / 32 rows), fed the oracle's o_lat."""
+    wl = WORKLOADS[2].with_(name=f"proj-b{B}", B=B, H=128 if B <= 33 else 32, n_max=40, len_lo=1, len_hi=40)
+    inp = make_inputs(wl)
+    ref = oracle.decode(inp)
+    print(f"[gpu] projections B={B}", flush=True)
+    dev = to_device(inp)
+    q_abs = ops.mla_absorb_q(dev["q_C"], dev["W_UK"])
+    o_lat = torch.from_numpy(ref["o_lat"].astype(np.float32)).to("cuda")
+    o = ops.mla_uv_out(o_lat, dev["W_UV"])
+    torch.cuda.synchronize()
+    e_q = oracle.relative_l2(q_abs.float().cpu().numpy().astype(np.float64), ref["q_abs"])
+    e_o = oracle.relative_l2(o.cpu().numpy().astype(np.float64), ref["o"])
+    print(f"[parity] projections B={B}: q_abs {e_q:.3e} o {e_o:.3e}", flush=True)
+    # q_abs is rounded once to bf16 (2^-9 relative); o is an fp32 product of exact inputs
+    assert e_q <= 4e-3 and e_o <= 1e-4
