@@ -9,9 +9,9 @@ bf16 caches and weights (``--config 3/4/5`` selects the other synthetic workload
 
 Timing: inputs are replicated into enough copies that consecutive steps never find their
 weights or cache in the 256 MB Infinity Cache (about 1 GB rotated); one HIP graph holds one step
-per copy and is replayed, so host launch overhead is not timed.  Per-kernel durations come from
-HIP events recorded around each kernel on the stream the kernels run on, after the stream has
-been primed so that the host runs ahead of the GPU.
+per copy and is replayed, so host launch overhead is not timed.  Per-kernel durations come from HIP events recorded
+on the launch stream around back-to-back launches of one kernel over the rotated copies, after
+the stream has been primed so that the host runs ahead of the GPU.
 """
 from __future__ import annotations
 
@@ -32,10 +32,19 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "k_absorb_bf16": "absorb_uv_mfma.hip",
+    "k_absorb_gemv": "absorb_uv_mfma.hip",
     "k_uv_bf16": "absorb_uv_mfma.hip",
+    "k_uv_gemv": "absorb_uv_mfma.hip",
     "k_partial_mfma": "decode_partial_mfma.hip",
-    "k_combine": "decode_generic.hip",
+    "k_combine_tiles": "decode_generic.hip",
 }
+
+
+def kernel_names(wl):
+    """Kernel that each pass launches for this workload (the library's own dispatch rules)."""
+    small = wl.B <= 4
+    return {"absorb": "k_absorb_gemv" if small else "k_absorb_bf16", "partial": "k_partial_mfma",
+            "combine": "k_combine_tiles", "uv": "k_uv_gemv" if small else "k_uv_bf16"}
 
 
 def parse():
@@ -191,35 +200,43 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / steps
     torch.cuda.synchronize()
 
-    # ---------------- per-kernel durations (HIP events around each launch)
+    # ---------------- per-kernel durations: HIP events around kernel_reps back-to-back launches of
+    # one kernel (rotating input copies, so weights and caches stay cold), on the launch stream
     names = ["absorb", "partial", "combine", "uv"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.kernel_reps)]
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(50_000_000)  # keep the GPU busy while the host enqueues everything below
-        for r in range(args.kernel_reps):
-            c = copies[r % R]
-            e = ev[r]
-            e[0].record(stream)
+    reps = args.kernel_reps
+
+    def launch(name, r):
+        c = copies[r % R]
+        if name == "absorb":
             ops.mla_absorb_q(c["q_C"], c["W_UK"], out=step.q_abs, stream=stream)
-            e[1].record(stream)
+        elif name == "partial":
             ops.mla_decode_partial(step.q_abs, c["q_R"], caches[r % R], c["lens"], wl.n_max, step.scale,
                                    step.workspace, num_splits=args.num_splits, stream=stream)
-            e[2].record(stream)
-            ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent, step.lse,
-                                   num_splits=args.num_splits, stream=stream)
-            e[3].record(stream)
+        elif name == "combine":
+            ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent,
+                                   step.lse, num_splits=args.num_splits, stream=stream)
+        else:
             ops.mla_uv_out(step.o_latent, c["W_UV"], out=step.out, stream=stream)
-            e[4].record(stream)
+
+    kern_us = {}
+    with torch.cuda.stream(stream):
+        for name in names:
+            ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(20_000_000)  # keep the GPU busy while the host enqueues the launches
+            ka.record(stream)
+            for r in range(reps):
+                launch(name, r)
+            kb.record(stream)
+            kb.synchronize()
+            kern_us[name] = ka.elapsed_time(kb) * 1e3 / reps
     torch.cuda.synchronize()
-    kern_us = {n: float(np.mean([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(1, args.kernel_reps)]) * 1e3)
-               for i, n in enumerate(names)}
 
     ab, per_tok = alg_bytes(wl, sum_len)
     af = alg_flops(wl, sum_len)
     step_bytes = sum(ab.values())
     value = sum_len / (ms_per_step * 1e-3)
     dom = max(names, key=lambda n: kern_us[n])
-    kname = {"absorb": "k_absorb_bf16", "partial": "k_partial_mfma", "combine": "k_combine", "uv": "k_uv_bf16"}[dom]
+    kname = kernel_names(wl)[dom]
     achieved_gbps = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),

@@ -129,7 +129,8 @@ int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, i
  */
 size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits);
 
-/* The number of partial-pass workgroups mla_decode_attn uses when num_splits == 0. */
+/* The number of partial-pass workgroups mla_decode_attn uses when num_splits == 0: about one per
+ * two 32-token tiles of the batch, ceil(B * ceil(max_len / 32) / 2), clamped to [1, 256]. */
 int mla_decode_auto_splits(int B, int H, int max_len);
 
 /*
@@ -151,8 +152,8 @@ int mla_decode_auto_splits(int B, int H, int max_len);
  *   max_len   host: an upper bound on every seq_lens[b]
  *   scale     softmax scale, positive and finite, normally 1/sqrt(d_h + d_R)
  *   workspace device buffer of at least mla_decode_workspace_bytes(...) bytes,
- *             any contents; overwritten
- *   o_latent  [B, H, d_c] float32 (written): sum_j a_j c_j
+ *             16-byte aligned, any contents; overwritten
+ *   o_latent  [B, H, d_c] float32, 16-byte aligned (written): sum_j a_j c_j
  *   lse       [B, H] float32 (written unless NULL): natural-log log-sum-exp of
  *             the scaled scores
  * A sequence with len 0 gives o_latent = 0 and lse = -inf.

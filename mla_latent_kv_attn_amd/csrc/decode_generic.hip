@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = tid + i * 256;
-        if (k < d_c) a.ws_acc[o * d_c + k] = acc[i];
+        if (k < d_c) a.ws_acc[ws_acc_index(slot, h, k, H, d_c)] = acc[i];
       }
       if (tid == 0) {
         a.ws_ml[o * 2 + 0] = m;
@@ -137,32 +137,41 @@ hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
 // Combine pass: for (b, h) merge the partials of the segments of sequence b.
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) acc_s / L,
 //   lse = (M + log2 L) * ln 2       (natural log).   No segment -> o = 0, lse = -inf.
-// Grid (H, B), 256 threads; thread t owns columns 2t + 512 j.  The segments of sequence b are the
-// partial-pass workgroups w0..w1 whose tile ranges meet b's tiles (prefix sums from the partial pass).
+// The segments of sequence b are the partial-pass workgroups w0..w1 whose tile ranges meet b's
+// tiles (tile prefix sums left in the workspace by the partial pass).
+// Grid (H, B, d_c / 128), 256 threads: the workgroup merges 128 columns.  The (m, l) pairs are
+// reduced by the whole workgroup and the segment weights 2^(m_s - M) kept in LDS (the first
+// kCombW of them); thread t then takes float4 column group t % 32 and segments t / 32 + 8 i,
+// four loads in flight, and the 8 segment groups are summed through LDS.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+constexpr int kCombW = 1024;
+
+__device__ __forceinline__ float block_reduce256(float v, bool is_max, float* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     const float u = __shfl_xor(v, d, 64);
     v = is_max ? fmaxf(v, u) : v + u;
   }
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  v = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
   return v;
 }
 
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  __shared__ float red[4];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
+  __shared__ float4 red[8][33];
+  __shared__ float wts[kCombW];
+  __shared__ float rr[4];
+  const int h = blockIdx.x, b = blockIdx.y, cq = blockIdx.z, tid = threadIdx.x;
   const int d_c = a.d_c, H = a.H;
+  const int c4 = tid & 31, sg = tid >> 5;
+  const int col = cq * 128 + 4 * c4;
   const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
   float* out = a.o_latent + ((int64_t)b * H + h) * d_c;
   if (Pb1 == Pb) {
-    for (int k = 2 * tid; k < d_c; k += 512) *(float2*)(out + k) = make_float2(0.f, 0.f);
-    if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
+    if (sg == 0 && col < d_c) *(float4*)(out + col) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse && tid == 0 && cq == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
     return;
   }
   const int Wp = min(a.W, NT);
@@ -170,52 +179,174 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int w0 = (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;
   const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
   const int nseg = w1 - w0 + 1;
-  const float* ml = a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2;   // segment s at ml + 2 H s
-  const int64_t mstride = 2 * (int64_t)H;
-
-  float M = -INFINITY;
-  for (int s = tid; s < nseg; s += blockDim.x) M = fmaxf(M, ml[s * mstride]);
-  M = block_reduce(M, true, red);
-  float Ls = 0.f;
-  for (int s = tid; s < nseg; s += blockDim.x) Ls += exp2f(ml[s * mstride] - M) * ml[s * mstride + 1];
-  Ls = block_reduce(Ls, false, red);
-  const float inv = 1.f / Ls;
-
-  const float* acc0 = a.ws_acc + ((int64_t)(w0 + b) * H + h) * d_c;   // segment s at acc0 + H d_c s
-  const int64_t astride = (int64_t)H * d_c;
-  for (int k = 2 * tid; k < d_c; k += 512) {
-    float2 o = make_float2(0.f, 0.f);
-    int s = 0;
-    for (; s + 4 <= nseg; s += 4) {
-      float2 v[4];
-      float f[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[u] = *(const float2*)(acc0 + (s + u) * astride + k);
-        f[u] = ml[(s + u) * mstride];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = exp2f(f[u] - M);
-        o.x = fmaf(wgt, v[u].x, o.x);
-        o.y = fmaf(wgt, v[u].y, o.y);
-      }
-    }
-    for (; s < nseg; ++s) {
-      const float2 v = *(const float2*)(acc0 + s * astride + k);
-      const float wgt = exp2f(ml[s * mstride] - M);
-      o.x = fmaf(wgt, v.x, o.x);
-      o.y = fmaf(wgt, v.y, o.y);
-    }
-    o.x *= inv;
-    o.y *= inv;
-    *(float2*)(out + k) = o;
+  const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml + H s
+  float mloc = -INFINITY;
+  for (int s = tid; s < nseg; s += 256) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
+  const float M = block_reduce256(mloc, true, rr);
+  float lloc = 0.f;
+  for (int s = tid; s < nseg; s += 256) {
+    const float2 v = ml[(int64_t)s * H];
+    const float f = exp2f(v.x - M);
+    if (s < kCombW) wts[s] = f;
+    lloc += f * v.y;
   }
-  if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
+  const float Ls = block_reduce256(lloc, false, rr);   // its barriers also publish wts
+  auto weight = [&](int s) -> float { return s < kCombW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M); };
+
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < d_c) {
+    const float* acc0 = a.ws_acc + ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at acc0 + H d_c s
+    const int64_t astride = (int64_t)H * d_c;
+    int s = sg;
+    for (; s + 24 < nseg; s += 32) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(acc0 + (s + 8 * u) * astride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = weight(s + 8 * u);
+        o.x = fmaf(f, v[u].x, o.x);
+        o.y = fmaf(f, v[u].y, o.y);
+        o.z = fmaf(f, v[u].z, o.z);
+        o.w = fmaf(f, v[u].w, o.w);
+      }
+    }
+    for (; s < nseg; s += 8) {
+      const float4 v = *(const float4*)(acc0 + s * astride);
+      const float f = weight(s);
+      o.x = fmaf(f, v.x, o.x);
+      o.y = fmaf(f, v.y, o.y);
+      o.z = fmaf(f, v.z, o.z);
+      o.w = fmaf(f, v.w, o.w);
+    }
+  }
+  red[sg][c4] = o;
+  __syncthreads();
+  if (sg == 0 && col < d_c) {
+    float4 t = red[0][c4];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      const float4 u = red[g][c4];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const float inv = 1.f / Ls;
+    *(float4*)(out + col) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
+  if (a.lse && tid == 0 && cq == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
+}
+
+// Combine for the tiled acc layout (H % 32 == 0, d_c % 32 == 0).  Grid (H/32, d_c/32, B), 1024
+// threads; the workgroup merges one 32-head x 32-column tile.  Its four groups of 256 threads take
+// every fourth segment; thread 64 v + l of a group reads float4 (v, l) of the tile (4 KiB
+// contiguous per segment), eight segments in flight, and the groups are summed through LDS.
+// (m, l) of the 32 heads: thread t takes head t % 32 and segments t / 32 + 32 i.
+constexpr int kCombWB = 128;   // segments whose weights are kept in LDS (the rest are recomputed)
+
+__global__ __launch_bounds__(1024) void k_combine_tiles(CombineArgs a) {
+  __shared__ float red[32][32];
+  __shared__ float Ms[32], Lsum[32];
+  __shared__ float wts[kCombWB][32];
+  __shared__ float4 part[3][256];
+  const int hb = blockIdx.x, cb = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int H = a.H, d_c = a.d_c;
+  const int grp = tid >> 8, t8 = tid & 255;
+  const int v = t8 >> 6, l = t8 & 63, r = l & 31;               // accumulator element (v, l): head r
+  const int hr = tid & 31, g = tid >> 5;                         // (m, l) phase: head hr, group g
+  const int head = hb * 32 + r;
+  const int col = cb * 32 + 8 * v + 4 * (l >> 5);
+  float* out = a.o_latent + ((int64_t)b * H + head) * d_c + col;
+  const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
+  if (Pb1 == Pb) {
+    if (grp == 0) *(float4*)out = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse && cb == 0 && tid < 32) a.lse[(int64_t)b * H + hb * 32 + tid] = -INFINITY;
+    return;
+  }
+  const int Wp = min(a.W, NT);
+  const int w0 = (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;   // owner of tile t: ceil((t+1)Wp/NT)-1
+  const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
+  const int nseg = w1 - w0 + 1;
+  const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + hb * 32) * 2);   // (s, head) at ml[s H + head]
+  float mloc = -INFINITY;
+  for (int s = g; s < nseg; s += 32) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
+  red[g][hr] = mloc;
+  __syncthreads();
+  if (tid < 32) {
+    float m = red[0][tid];
+    for (int i = 1; i < 32; ++i) m = fmaxf(m, red[i][tid]);
+    Ms[tid] = m;
+  }
+  __syncthreads();
+  {
+    const float M = Ms[hr];
+    float lloc = 0.f;
+    for (int s = g; s < nseg; s += 32) {
+      const float2 q = ml[(int64_t)s * H + hr];
+      const float f = exp2f(q.x - M);
+      if (s < kCombWB) wts[s][hr] = f;
+      lloc += f * q.y;
+    }
+    red[g][hr] = lloc;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float t = red[0][tid];
+    for (int i = 1; i < 32; ++i) t += red[i][tid];
+    Lsum[tid] = t;
+  }
+  __syncthreads();
+  const float M = Ms[r];
+  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
+  const float* src = a.ws_acc + (((int64_t)(w0 + b) * (H >> 5) + hb) * (d_c >> 5) + cb) * 1024 + 256 * v + 4 * l;
+  auto weight = [&](int s) -> float { return s < kCombWB ? wts[s][r] : exp2f(ml[(int64_t)s * H + r].x - M); };
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = grp;
+  for (; s + 28 < nseg; s += 32) {
+    float4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *(const float4*)(src + (s + 4 * u) * sstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = weight(s + 4 * u);
+      o.x = fmaf(f, x[u].x, o.x);
+      o.y = fmaf(f, x[u].y, o.y);
+      o.z = fmaf(f, x[u].z, o.z);
+      o.w = fmaf(f, x[u].w, o.w);
+    }
+  }
+  for (; s < nseg; s += 4) {
+    const float4 x = *(const float4*)(src + s * sstride);
+    const float f = weight(s);
+    o.x = fmaf(f, x.x, o.x);
+    o.y = fmaf(f, x.y, o.y);
+    o.z = fmaf(f, x.z, o.z);
+    o.w = fmaf(f, x.w, o.w);
+  }
+  if (grp > 0) part[grp - 1][t8] = o;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const float4 u = part[i][t8];
+      o.x += u.x;
+      o.y += u.y;
+      o.z += u.z;
+      o.w += u.w;
+    }
+    const float inv = 1.f / Lsum[r];
+    *(float4*)out = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (a.lse && cb == 0 && tid < 32)
+      a.lse[(int64_t)b * H + hb * 32 + tid] = (Ms[tid] + log2f(Lsum[tid])) * 0.69314718055994530942f;
+  }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(256), 0, s, a);
+  if (ws_blocked(a.H, a.d_c))
+    hipLaunchKernelGGL(k_combine_tiles, dim3(a.H / 32, a.d_c / 32, a.B), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_combine_rows, dim3(a.H, a.B, (a.d_c + 127) / 128), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

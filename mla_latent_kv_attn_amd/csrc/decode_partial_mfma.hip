@@ -151,16 +151,27 @@ void k_partial_mfma(PartialArgs a) {
   const uint32_t voff_x0 = (uint32_t)lane * 16u, voff_x1 = (uint32_t)(lane ^ 1) * 16u;
   const uint32_t voff_f8_0 = (uint32_t)((lane & 31)) * 16u, voff_f8_1 = (uint32_t)((lane & 31) ^ 1) * 16u;
   int lb = seq_of_tile(P, a.B, t_begin);
-  auto issue = [&](int it) {
-    // opaque copies: keep the 32-bit lane offsets from being folded into hoisted 64-bit pointers
-    uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
-    asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+  // A tile's loads are LPT "jobs" per wave: latent rows (bf16) or row pairs (fp8), then the
+  // fp8 scale rows, then the rope chunks.  prep() resolves where tile it lives; job(k) issues
+  // load k.  In the tile loop the jobs of tile it + 2 are spread over the score k-steps of tile
+  // it, so that a stall on a full memory queue overlaps the MFMAs in flight.
+  constexpr int kLatJobs = FP8 ? 16 / NWAVE : 32 / NWAVE;
+  constexpr int kScaleJobs = FP8 ? 4 / NWAVE : 0;
+  struct TileSrc {
+    const uint8_t* lbase;   // byte address of row 0 of the tile's latents
+    const uint8_t* rbase;   // same for the rope keys
+    const float* sbase;     // fp8: scale of row 0
+    uint32_t st;            // LDS address of the stage
+    int last;               // last valid row of the tile
+  };
+  auto prep = [&](int it) -> TileSrc {
     const int t = t_begin + it;
     while (t >= P[lb + 1]) ++lb;
     const int b = __builtin_amdgcn_readfirstlane(lb);
     const int tok0 = (t - P[b]) * kTile;
-    const int last = min(kTile, L[b] - tok0) - 1;  // last valid row of the tile
-    const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (it % kNst) * LY::kStage);
+    TileSrc ts;
+    ts.last = min(kTile, L[b] - tok0) - 1;
+    ts.st = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (it % kNst) * LY::kStage);
     int64_t lrow0, rrow0, srow0;  // element offsets of the page / sequence holding the tile
     int tslot0;                   // row of tok0 inside it
     if (PAGED) {
@@ -175,45 +186,49 @@ void k_partial_mfma(PartialArgs a) {
       srow0 = (int64_t)b * a.scale_sb;
       tslot0 = tok0;
     }
-    // byte address of row 0 of the tile; rows advance by the token stride (a 32-bit offset)
-    const uint8_t* lbase = latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * (FP8 ? 1 : 2);
+    ts.lbase = latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * (FP8 ? 1 : 2);
+    ts.rbase = rope + (rrow0 + (int64_t)tslot0 * a.rope_st) * 2;
+    ts.sbase = FP8 ? a.lscale + srow0 + tslot0 : nullptr;
+    return ts;
+  };
+  // vx0, vx1, vf0, vf1: opaque copies of the lane offsets (made by the caller), which keep them
+  // from being folded into hoisted 64-bit pointers
+  auto job = [&](const TileSrc& ts, int k, uint32_t vx0, uint32_t vx1, uint32_t vf0, uint32_t vf1) {
     const uint32_t lstride = (uint32_t)a.lat_st * (FP8 ? 1u : 2u);
-    if (!FP8) {
-#pragma unroll
-      for (int i = 0; i < 32 / NWAVE; ++i) {
-        const int r = wave + NWAVE * i;
+    const int last = ts.last;
+    if (k < kLatJobs) {
+      if (!FP8) {
+        const int r = wave + NWAVE * k;
         const uint32_t roff = (uint32_t)min(r, last) * lstride;
-        lds_dma16(lbase, (((r >> 3) & 1) ? vx1 : vx0) + roff, st + r * kLatStride);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16 / NWAVE; ++i) {
-        const int pr = wave + NWAVE * i;       // row pair
+        lds_dma16(ts.lbase, (((r >> 3) & 1) ? vx1 : vx0) + roff, ts.st + r * kLatStride);
+      } else {
+        const int pr = wave + NWAVE * k;       // row pair
         const uint32_t r0 = (uint32_t)min(2 * pr, last) * lstride;
         const uint32_t r1 = (uint32_t)min(2 * pr + 1, last) * lstride;
-        lds_dma16(lbase, (lane >> 5) ? r1 + vf1 : r0 + vf0, st + pr * kLatStride);
+        lds_dma16(ts.lbase, (lane >> 5) ? r1 + vf1 : r0 + vf0, ts.st + pr * kLatStride);
       }
-#pragma unroll
-      for (int i = 0; i < 4 / NWAVE; ++i) {
-        const int q = wave + NWAVE * i;        // rows 8q .. 8q+7
-        if (lane < 8) {
-          const int tok_u = tslot0 + min(8 * q, last);
-          const int dr = min(8 * q + lane, last) - min(8 * q, last);
-          lds_dma4(a.lscale + srow0 + tok_u, (uint32_t)dr * 4u, st + LY::kScaleOff + 32 * q);
-        }
+    } else if (k < kLatJobs + kScaleJobs) {
+      const int q = wave + NWAVE * (k - kLatJobs);   // rows 8q .. 8q+7
+      if (lane < 8) {
+        const int dr = min(8 * q + lane, last);
+        lds_dma4(ts.sbase, (uint32_t)dr * 4u, ts.st + LY::kScaleOff + 32 * q);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 4 / NWAVE; ++i) {
+    } else {
       // rope region is chunk-major: slot (c, r) = 32c + r holds bytes [16c, 16c+16) of row r;
-      // instruction q writes chunks 2q and 2q+1 of all 32 rows
-      const int q = wave + NWAVE * i;
+      // job q writes chunks 2q and 2q+1 of all 32 rows
+      const int q = wave + NWAVE * (k - kLatJobs - kScaleJobs);
       const int r = lane & 31;
       const int c = 2 * q + (lane >> 5);
       const int dr = min(r, last);
-      const uint8_t* gb = rope + (rrow0 + (int64_t)tslot0 * a.rope_st) * 2;
-      lds_dma16(gb, (uint32_t)(dr * (int)a.rope_st * 2 + c * 16), st + LY::kRopeOff + 1024 * q);
+      lds_dma16(ts.rbase, (uint32_t)(dr * (int)a.rope_st * 2 + c * 16), ts.st + LY::kRopeOff + 1024 * q);
     }
+  };
+  auto issue = [&](int it) {
+    const TileSrc ts = prep(it);
+    uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
+    asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+#pragma unroll
+    for (int k = 0; k < LPT; ++k) job(ts, k, vx0, vx1, vf0, vf1);
   };
 
   // ---------------------------------------------------------------- per-lane constants
@@ -290,7 +305,15 @@ void k_partial_mfma(PartialArgs a) {
       if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
-      if (it + 2 < ntiles) issue(it + 2);
+      // spread the next tile's loads over the score k-steps (one wave per workgroup issues all
+      // 36 at once: spread, their addresses would not fit in its registers)
+      constexpr bool kSpread = NWAVE >= 2;
+      const bool pre = it + 2 < ntiles;
+      TileSrc nxt;
+      if (pre) {
+        if (kSpread) nxt = prep(it + 2);
+        else issue(it + 2);
+      }
 
       const int nvalid = min(kTile, len_b - (t_begin + it - P[b]) * kTile);
       const uint8_t* st = smem + (it % kNst) * LY::kStage;
@@ -321,6 +344,12 @@ void k_partial_mfma(PartialArgs a) {
           n1 = lat_op(s + 3);
         }
         asm volatile("" ::: "memory");
+        if (kSpread && pre && (s / 2) * LPT / 16 < (s / 2 + 1) * LPT / 16) {
+          uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
+          asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+#pragma unroll
+          for (int k = (s / 2) * LPT / 16; k < (s / 2 + 1) * LPT / 16; ++k) job(nxt, k, vx0, vx1, vf0, vf1);
+        }
         // two accumulators: consecutive MFMAs are independent (a dependent 32x32x16 chain issues
         // at roughly 60% of the independent rate)
         const u32x4 q0 = (s < QREG) ? qf[s < QREG ? s : 0] : q_lds(s);
@@ -470,15 +499,17 @@ void k_partial_mfma(PartialArgs a) {
       // loop (where they would occupy registers for the whole tile loop)
       int ln = lane;
       asm volatile("" : "+v"(ln));
+      // tiled workspace layout: each accumulator register block is one 4 KiB tile (32 heads x
+      // 32 columns) stored as-is, one contiguous KiB per store instruction
 #pragma unroll
       for (int hb = 0; hb < NWAVE; ++hb) {
-        float* dst = a.ws_acc + (slot + hb * 32 + (ln & 31)) * 512 + 32 * wave * CPW + 4 * (ln >> 5);
+        float* dst = a.ws_acc + ((int64_t)(w + b) * NWAVE + hb) * 16 * 1024 + wave * CPW * 1024 + 4 * ln;
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
             const f32x16& A = acc[hb * CPW + j];
-            *(f32x4*)(dst + 32 * j + 8 * v4) = f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
+            *(f32x4*)(dst + 1024 * j + 256 * v4) = f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
           }
         }
       }

@@ -21,10 +21,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Partial-pass workgroups when the caller passes 0: one workgroup per CU for large batches
 // (the kernel runs one workgroup per CU), fewer for short single-sequence work so that each
 // workgroup owns at least four 32-token tiles.
+// About two 32-token tiles per workgroup, at most one workgroup per CU (256).  At small batch
+// the partial pass is latency-bound and more splits shorten it, until the combine pass's reads
+// of the (W + B - 1) x H x d_c partials outweigh the gain (measured at B = 1, N = 4096: 64 splits).
 int auto_splits(int B, int H, int max_len) {
   (void)H;
   const int64_t nt = (int64_t)B * ((max_len + mla::kTile - 1) / mla::kTile);
-  int64_t w = nt / 4;
+  int64_t w = (nt + 1) / 2;
   if (w > 256) w = 256;
   if (w < 1) w = 1;
   return (int)w;
@@ -112,6 +115,7 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   if (W > 65535) return MLA_ERR_SHAPE;
   const size_t need = mla::ws_total_bytes(W, B, H, d_c);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
 
   if (q_dtype == MLA_F32 && cache->latent_dtype == MLA_F32 && cache->rope_dtype == MLA_F32) {
     if (d_c > 1024 || d_R > 256) return MLA_ERR_UNSUPPORTED;
@@ -175,6 +179,7 @@ int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c,
   if (W > 65535) return MLA_ERR_SHAPE;
   const size_t need = mla::ws_total_bytes(W, B, H, d_c);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(o_latent)) return MLA_ERR_UNSUPPORTED;
   ca->seq_lens = seq_lens;
   ca->B = B;
   ca->H = H;

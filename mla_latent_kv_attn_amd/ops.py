@@ -189,3 +189,4 @@ def mla_uv_out(o_latent: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.T
     check("mla_uv_out", _lib.lib().mla_uv_out(o_latent.data_ptr(), W_UV.data_ptr(), dtype_code(W_UV),
                                               out.data_ptr(), B, H, d_h, d_c, _stream(stream, o_latent)))
     return out
+

@@ -60,8 +60,10 @@ def test_workspace_size_formula(lib):
         ml = (slots * H * 2 * 4 + 255) // 256 * 256
         prefix = ((B + 1) * 4 + 255) // 256 * 256
         assert ws(B, H, d_c, N, S) == acc + ml + prefix
-    # the auto choice: about four 32-token tiles per workgroup, at most 256 workgroups
-    assert lib.mla_decode_auto_splits(1, 128, 4096) == 32
+    # the auto choice: about two 32-token tiles per workgroup, at most 256 workgroups
+    assert lib.mla_decode_auto_splits(1, 128, 4096) == 64
+    assert lib.mla_decode_auto_splits(1, 128, 4095) == 64
+    assert lib.mla_decode_auto_splits(1, 128, 64) == 1
     assert lib.mla_decode_auto_splits(64, 128, 8192) == 256
     assert lib.mla_decode_auto_splits(1, 128, 1) == 1
 
@@ -101,6 +103,8 @@ def test_decode_attn_validation(lib):
     assert _attn(lib, d, ws=None) == L.MLA_ERR_WORKSPACE
     need = lib.mla_decode_workspace_bytes(1, 128, 512, 4096, 0)
     assert _attn(lib, d, ws_bytes=need - 1) == L.MLA_ERR_WORKSPACE
+    assert _attn(lib, d, ws=FAKE + 8) == L.MLA_ERR_UNSUPPORTED           # workspace not 16-byte aligned
+    assert _attn(lib, d, out=FAKE + 4) == L.MLA_ERR_UNSUPPORTED          # o_latent not 16-byte aligned
     assert _attn(lib, d, d_c=256) == L.MLA_ERR_UNSUPPORTED               # bf16 path is d_c = 512 only
     assert _attn(lib, d, H=96) == L.MLA_ERR_UNSUPPORTED
     assert _attn(lib, _desc(latent=FAKE + 2)) == L.MLA_ERR_UNSUPPORTED   # misaligned rows
@@ -128,3 +132,4 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(L.MlaLibraryError):
         L.lib()
+

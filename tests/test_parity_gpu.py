@@ -215,6 +215,7 @@ def test_graph_capture_replays_match_eager():
     inp = make_inputs(wl, lens=np.array(lens))
     dev = to_device(inp)
     cache = device_cache(inp, dev)
+    print("[gpu] graph capture", flush=True)
     step = DecodeStep(wl.B, wl.H, wl.d_h, wl.d_c, wl.d_R, wl.n_max, torch.bfloat16, "cuda", num_splits=3)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
