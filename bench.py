@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -134,6 +136,25 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration > 0:
+        # plain device-to-device copies of a buffer well above the 256 MB Infinity Cache: the
+        # reference for the HBM byte counters, and the practical read+write bandwidth ceiling
+        n = int(args.copy_calibration * 1e6) // 16 * 16
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ca.record()
+        for _ in range(4):
+            dst.copy_(src)
+        cb.record()
+        cb.synchronize()
+        ms = ca.elapsed_time(cb) / 4
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5, "copy_ms": round(ms, 4),
+                          "read_plus_write_TBps": round(2 * n / (ms * 1e-3) / 1e12, 3)}), flush=True)
+        return
 
     from mla_latent_kv_attn_amd import ops
     from mla_latent_kv_attn_amd.step import DecodeStep

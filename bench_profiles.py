@@ -1,0 +1,135 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 output of bench.py runs into the short summaries kept under profiles/.
+
+  python bench_profiles.py stats --csv <kernel_stats.csv> --bench <bench stdout> --cmd "<command>"
+                                 --out profiles/<kernel>_<workload>_kernel_stats.txt
+  python bench_profiles.py pmc --kernel k_partial_mfma --workload v3-b1 --fetch <csv> --write <csv>
+                               --cal-fetch <csv> --cal-write <csv> --cal-bytes N --cmd "<commands>"
+
+The pmc form reads per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of one kernel from two separate
+counter runs, scales each by what the same counter reads for a plain device copy of known size
+(copy kernels read and write exactly N bytes), and writes profiles/<kernel>_<workload>_pmc.json
+(HBM bytes per launch, keyed to the kernel source it was measured on) plus a .txt summary.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(f"none of {names} in {list(row)}")
+
+
+def counter_per_dispatch(path, counter, kernel_substr):
+    """Mean counter value over the dispatches whose kernel name contains kernel_substr."""
+    vals = {}
+    for r in _rows(path):
+        if _col(r, "Counter_Name", "counter_name") != counter:
+            continue
+        if kernel_substr not in _col(r, "Kernel_Name", "kernel_name"):
+            continue
+        d = _col(r, "Dispatch_Id", "dispatch_id")
+        vals[d] = vals.get(d, 0.0) + float(_col(r, "Counter_Value", "counter_value"))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {kernel_substr!r}")
+    return statistics.mean(vals.values()), len(vals)
+
+
+def cmd_stats(a):
+    rows = _rows(a.csv)
+    bench = None
+    with open(a.bench) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    lines = [f"# rocprofv3 kernel-trace summary: {a.title}", "", "Command:", "", "    " + a.cmd, "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = _col(r, "Name", "KernelName", "Kernel_Name")
+        if name.startswith("__amd") or "elementwise" in name or "spin_kernel" in name or "fill" in name:
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| {short} | {_col(r, 'Calls')} | {float(_col(r, 'AverageNs')) / 1e3:.2f} | "
+                     f"{float(_col(r, 'MinNs')) / 1e3:.2f} | {float(_col(r, 'MaxNs')) / 1e3:.2f} | "
+                     f"{float(_col(r, 'Percentage')):.1f} |")
+    if bench:
+        lines += ["", "bench.py line of the same run (HIP-event averages, us): " + json.dumps(bench["kernels_us"]),
+                  f"ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
+                  f"roofline {json.dumps(bench['roofline'])}"]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_pmc(a):
+    from bench import KERNEL_SOURCES, source_hash
+    fetch_kib, n1 = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write_kib, n2 = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    cal_f, _ = counter_per_dispatch(a.cal_fetch, "FETCH_SIZE", a.cal_kernel)
+    cal_w, _ = counter_per_dispatch(a.cal_write, "WRITE_SIZE", a.cal_kernel)
+    kf = a.cal_bytes / (cal_f * 1024.0)     # true bytes per counted byte, reads
+    kw = a.cal_bytes / (cal_w * 1024.0)     # same, writes
+    fetch_b = fetch_kib * 1024.0 * kf
+    write_b = write_kib * 1024.0 * kw
+    out = {"kernel": a.kernel, "workload": a.workload, "source_hash": source_hash(KERNEL_SOURCES[a.kernel]),
+           "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+           "dispatches": [n1, n2], "copy_scale_fetch": kf, "copy_scale_write": kw,
+           "hbm_bytes_per_launch": round(fetch_b + write_b), "hbm_read_bytes": round(fetch_b),
+           "hbm_write_bytes": round(write_b), "commands": a.cmd}
+    base = os.path.join(ROOT, "profiles", f"{a.kernel}_{a.workload}_pmc")
+    with open(base + ".json", "w") as f:
+        json.dump(out, f, indent=1)
+    txt = [f"# rocprofv3 counters: {a.kernel} on {a.workload}", "", "Commands:", ""]
+    txt += ["    " + c for c in a.cmd.split(" ;; ")]
+    txt += ["", f"FETCH_SIZE {fetch_kib:.1f} KiB/dispatch ({n1} dispatches), WRITE_SIZE {write_kib:.1f} KiB/dispatch "
+                f"({n2} dispatches)",
+            f"copy calibration ({a.cal_bytes} B read + written by {a.cal_kernel}): FETCH_SIZE scale {kf:.4f}, "
+            f"WRITE_SIZE scale {kw:.4f}",
+            f"HBM bytes per launch: read {fetch_b:.0f}, write {write_b:.0f}, total {fetch_b + write_b:.0f}"]
+    with open(base + ".txt", "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--bench", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="")
+    s.add_argument("--out", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("--kernel", required=True)
+    p.add_argument("--workload", required=True)
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--cal-fetch", required=True)
+    p.add_argument("--cal-write", required=True)
+    p.add_argument("--cal-bytes", type=int, required=True)
+    p.add_argument("--cal-kernel", default="copy")
+    p.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    cmd_stats(a) if a.what == "stats" else cmd_pmc(a)
+
+
+if __name__ == "__main__":
+    main()
