@@ -9,9 +9,12 @@
 // Design (one workgroup per CU, NWAVE = H/32 waves, wave w owns heads 32w .. 32w+31):
 //  * The batch's token tiles (32 tokens) are split evenly over the workgroups (see
 //    mla_internal.h).  A workgroup streams its tiles through a 3-stage LDS ring filled by
-//    direct global->LDS loads (global_load_lds_dwordx4), so a tile arrives two tiles ahead of its
-//    use without passing through registers.  Every tile is read from HBM once and shared by all
-//    heads of the workgroup.
+//    direct global->LDS loads (global_load_lds_dwordx4), without passing through registers:
+//    while tile it is scored, tile it-1 is still being read by the value step and tile it+1 is
+//    in flight.  Every tile is read from HBM once and shared by all heads of the workgroup.
+//  * Software pipeline, one barrier per tile: score(it), value(it-1), softmax(it) form one basic
+//    block, so the VALU work of the softmax overlaps the value MFMAs of the previous tile; the
+//    probabilities, rescale factors and flags are double-buffered by tile parity.
 //  * Score block per wave: S^T[32 tokens x 32 heads] = C_tile[32 x 576] . Qhat^T[576 x 32],
 //    36 MFMA 32x32x16 steps.  Qhat = [q' ; q_R] of the wave's 32 heads stays in registers for the
 //    whole segment.
@@ -100,6 +103,8 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* p) {
 }
 
 constexpr int lgkmcnt_imm0() { return 15 | (3 << 14) | (7 << 4); }
+// s_waitcnt immediate waiting for vmcnt == 0 and lgkmcnt == 0 (tile loads landed, own LDS writes done)
+constexpr int vm_lgkm_imm0() { return 7 << 4; }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -117,17 +122,17 @@ void k_partial_mfma(PartialArgs a) {
   static_assert(LPT < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNst * LY::kStage];
   __shared__ int P[kMaxB + 1];
-  __shared__ int L[kMaxB];
   __shared__ __attribute__((aligned(16))) uint8_t qrs[NWAVE * 32 * 128];  // q_R of each wave's heads
   // fp8 variant: the last (32 - QREG) latent k-steps of Qhat live in LDS (its tiles are half the
   // size of bf16 tiles, which leaves room), freeing registers for the fp8 widening
-  constexpr int QREG = FP8 ? 24 : 32;
+  constexpr int QREG = FP8 ? (NWAVE == 1 ? 20 : 24) : 32;
   __shared__ __attribute__((aligned(16))) uint8_t qls[FP8 ? NWAVE * (32 - QREG) * 1024 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[NWAVE * 32 * kPbStride];  // bf16 probabilities
-  __shared__ float alpha_s[NWAVE * 32];   // rescale factor of each head (valid when its flag is set)
-  __shared__ int flags_s[NWAVE];          // 1 if the wave's heads were rescaled this tile
+  // double-buffered by tile parity: tile it writes buffer it & 1 while tile it-1's is being read
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][NWAVE * 32 * kPbStride];  // bf16 probabilities
+  __shared__ float alpha_s[2][NWAVE * 32];   // rescale factor of each head
+  __shared__ __attribute__((aligned(16))) int flags_s[2][4];   // 1 if any of wave w's heads was rescaled
 
-  build_tile_prefix(a.seq_lens, a.B, P, L);
+  build_tile_prefix(a.seq_lens, a.B, P, nullptr);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
   const int NT = P[a.B];
@@ -150,11 +155,17 @@ void k_partial_mfma(PartialArgs a) {
   // per-lane byte offsets of the DMA loads (16-byte chunk positions, XOR-swizzled)
   const uint32_t voff_x0 = (uint32_t)lane * 16u, voff_x1 = (uint32_t)(lane ^ 1) * 16u;
   const uint32_t voff_f8_0 = (uint32_t)((lane & 31)) * 16u, voff_f8_1 = (uint32_t)((lane & 31) ^ 1) * 16u;
-  int lb = seq_of_tile(P, a.B, t_begin);
+  // Load cursor (uniform): the sequence lk_b of the next tile to load, its first tile lk_start,
+  // the first tile of the sequence after it lk_next, and its length lk_len.
+  int lk_b = seq_of_tile(P, a.B, t_begin);
+  int lk_start = __builtin_amdgcn_readfirstlane(P[lk_b]);
+  int lk_next = __builtin_amdgcn_readfirstlane(P[lk_b + 1]);
+  int lk_len = load_uniform_i32(a.seq_lens + lk_b);
   // A tile's loads are LPT "jobs" per wave: latent rows (bf16) or row pairs (fp8), then the
-  // fp8 scale rows, then the rope chunks.  prep() resolves where tile it lives; job(k) issues
-  // load k.  In the tile loop the jobs of tile it + 2 are spread over the score k-steps of tile
-  // it, so that a stall on a full memory queue overlaps the MFMAs in flight.
+  // fp8 scale rows, then the rope chunks.  advance() moves the cursor to the sequence of a tile
+  // (a branch taken only at sequence ends); locate() computes where the tile lives (straight-line
+  // code, so that its scalar loads can be scheduled under the MFMAs of the tile loop); job(k)
+  // issues load k.
   constexpr int kLatJobs = FP8 ? 16 / NWAVE : 32 / NWAVE;
   constexpr int kScaleJobs = FP8 ? 4 / NWAVE : 0;
   struct TileSrc {
@@ -164,13 +175,21 @@ void k_partial_mfma(PartialArgs a) {
     uint32_t st;            // LDS address of the stage
     int last;               // last valid row of the tile
   };
-  auto prep = [&](int it) -> TileSrc {
+  auto advance = [&](int it) __attribute__((always_inline)) {
     const int t = t_begin + it;
-    while (t >= P[lb + 1]) ++lb;
-    const int b = __builtin_amdgcn_readfirstlane(lb);
-    const int tok0 = (t - P[b]) * kTile;
+    while (t >= lk_next) {
+      ++lk_b;
+      lk_start = lk_next;
+      lk_next = __builtin_amdgcn_readfirstlane(P[lk_b + 1]);
+      lk_len = load_uniform_i32(a.seq_lens + lk_b);
+    }
+  };
+  auto locate = [&](int it) __attribute__((always_inline)) -> TileSrc {
+    const int t = t_begin + it;
+    const int b = __builtin_amdgcn_readfirstlane(lk_b);
+    const int tok0 = (t - lk_start) * kTile;
     TileSrc ts;
-    ts.last = min(kTile, L[b] - tok0) - 1;
+    ts.last = min(kTile, lk_len - tok0) - 1;
     ts.st = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (it % kNst) * LY::kStage);
     int64_t lrow0, rrow0, srow0;  // element offsets of the page / sequence holding the tile
     int tslot0;                   // row of tok0 inside it
@@ -186,14 +205,20 @@ void k_partial_mfma(PartialArgs a) {
       srow0 = (int64_t)b * a.scale_sb;
       tslot0 = tok0;
     }
-    ts.lbase = latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * (FP8 ? 1 : 2);
-    ts.rbase = rope + (rrow0 + (int64_t)tslot0 * a.rope_st) * 2;
-    ts.sbase = FP8 ? a.lscale + srow0 + tslot0 : nullptr;
+    ts.lbase = (const uint8_t*)uniform_ptr(latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * (FP8 ? 1 : 2));
+    ts.rbase = (const uint8_t*)uniform_ptr(rope + (rrow0 + (int64_t)tslot0 * a.rope_st) * 2);
+    ts.sbase = FP8 ? (const float*)uniform_ptr(a.lscale + srow0 + tslot0) : nullptr;
+    ts.last = __builtin_amdgcn_readfirstlane(ts.last);
     return ts;
   };
+  auto prep = [&](int it) __attribute__((always_inline)) -> TileSrc {
+    advance(it);
+    return locate(it);
+  };
+
   // vx0, vx1, vf0, vf1: opaque copies of the lane offsets (made by the caller), which keep them
   // from being folded into hoisted 64-bit pointers
-  auto job = [&](const TileSrc& ts, int k, uint32_t vx0, uint32_t vx1, uint32_t vf0, uint32_t vf1) {
+  auto job = [&](const TileSrc& ts, int k, uint32_t vx0, uint32_t vx1, uint32_t vf0, uint32_t vf1) __attribute__((always_inline)) {
     const uint32_t lstride = (uint32_t)a.lat_st * (FP8 ? 1u : 2u);
     const int last = ts.last;
     if (k < kLatJobs) {
@@ -223,13 +248,16 @@ void k_partial_mfma(PartialArgs a) {
       lds_dma16(ts.rbase, (uint32_t)(dr * (int)a.rope_st * 2 + c * 16), ts.st + LY::kRopeOff + 1024 * q);
     }
   };
-  auto issue = [&](int it) {
-    const TileSrc ts = prep(it);
+  auto issue_src = [&](TileSrc ts) __attribute__((always_inline)) {
+    // opaque here: keeps the per-lane addresses derived from ts from being computed early and
+    // held in registers across the tile loop
+    asm volatile("" : "+s"(ts.lbase), "+s"(ts.rbase), "+s"(ts.sbase), "+s"(ts.st), "+s"(ts.last));
     uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
     asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
 #pragma unroll
     for (int k = 0; k < LPT; ++k) job(ts, k, vx0, vx1, vf0, vf1);
-  };
+  };  auto issue = [&](int it) __attribute__((always_inline)) { issue_src(prep(it)); };
+
 
   // ---------------------------------------------------------------- per-lane constants
   constexpr int CPW = 16 / NWAVE;           // 32-column blocks of the latent owned by each wave
@@ -261,8 +289,214 @@ void k_partial_mfma(PartialArgs a) {
   const int qr_base = 16 * (hf * 32 + (lane & 31));
   const int pb_base = (lane & 31) * kPbStride + 16 * hf;
 
+  // ---------------------------------------------------------------- phases of one tile
+  // score: S^T block of this wave's 32 heads for the tile in stage `st` (latent and rope parts
+  // summed; fp8: the latent part multiplied by the per-token scale)
+  u32x4 qf[QREG];
+  using LatRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
+  auto widen = [&](const LatRaw& r) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (!FP8) return r;
+    else return fp8x8_to_bf16x8(r);
+  };
+  // score(st, jobs, js): with jobs = true_type the loads of the tile described by js are issued
+  // between the MFMAs (each load instruction takes tens of cycles to issue; there the MFMAs in
+  // flight cover it)
+  auto score = [&](const uint8_t* st, auto jobs, TileSrc js) __attribute__((always_inline)) -> f32x16 {
+    constexpr bool kJobs = decltype(jobs)::value;
+    if (kJobs) asm volatile("" : "+s"(js.lbase), "+s"(js.rbase), "+s"(js.sbase), "+s"(js.st), "+s"(js.last));
+    f32x16 S = {}, S2 = {};
+    // latent score operand: bf16 rows read as 16 bytes; fp8 rows read as 8 raw bytes and widened
+    // to bf16 just before the MFMA that consumes them (keeps prefetched operands small)
+    auto lat_op = [&](int s) __attribute__((always_inline)) -> LatRaw {
+      if constexpr (!FP8) return *(const u32x4*)(st + sc_base + 32 * s);
+      else return *(const u32x2*)(st + ((s & 1) ? sc_base_odd : sc_base) + 16 * s);
+    };
+    auto rope_op = [&](int q) __attribute__((always_inline)) -> u32x4 { return *(const u32x4*)(st + rope_base + 1024 * q); };
+    auto q_lds = [&](int s) __attribute__((always_inline)) -> u32x4 {
+      return *(const u32x4*)(qls + wave * (32 - QREG) * 1024 + qr_base + 1024 * (s - QREG));
+    };
+    // operands of k-steps s .. s + kPre - 1 are in flight while the MFMAs of step s issue
+    constexpr int kPre = 4;
+    LatRaw pre[kPre];
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) pre[s] = lat_op(s);
+#pragma unroll
+    for (int s = 0; s < 32; s += 2) {
+      const LatRaw a0 = pre[s % kPre], a1 = pre[(s + 1) % kPre];
+      if (s + kPre < 32) {
+        pre[s % kPre] = lat_op(s + kPre);
+        pre[(s + 1) % kPre] = lat_op(s + kPre + 1);
+      }
+      asm volatile("" ::: "memory");
+      // two accumulators: consecutive MFMAs are independent (a dependent 32x32x16 chain issues
+      // at roughly 60% of the independent rate)
+      const u32x4 q0 = (s < QREG) ? qf[s < QREG ? s : 0] : q_lds(s);
+      const u32x4 q1 = (s + 1 < QREG) ? qf[s + 1 < QREG ? s + 1 : 0] : q_lds(s + 1);
+      S = mfma32x32x16(widen(a0), q0, S);
+      S2 = mfma32x32x16(widen(a1), q1, S2);
+      if constexpr (kJobs) {
+        const int k0 = (s / 2) * LPT / 16, k1 = (s / 2 + 1) * LPT / 16;   // constants after unrolling
+        if (k0 < k1) {
+          uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
+          asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+#pragma unroll
+          for (int k = k0; k < k1; ++k) job(js, k, vx0, vx1, vf0, vf1);
+        }
+      }
+    }
+    {
+      // rope k-steps: A = rope keys of the tile, B = q_R of the wave's heads (both LDS)
+      const uint8_t* qrow = qrs + wave * 4096 + qr_base;
+      const u32x4 b0 = *(const u32x4*)(qrow);
+      const u32x4 b1 = *(const u32x4*)(qrow + 1024);
+      const u32x4 b2 = *(const u32x4*)(qrow + 2048);
+      const u32x4 b3 = *(const u32x4*)(qrow + 3072);
+      const u32x4 r0 = rope_op(0), r1 = rope_op(1), r2 = rope_op(2), r3 = rope_op(3);
+      if (FP8) {
+        S += S2;  // latent part (scaled per token below); rope part accumulates in S2
+        S2 = f32x16{};
+        S2 = mfma32x32x16(r0, b0, S2);
+        S2 = mfma32x32x16(r1, b1, S2);
+        S2 = mfma32x32x16(r2, b2, S2);
+        S2 = mfma32x32x16(r3, b3, S2);
+      } else {
+        S = mfma32x32x16(r0, b0, S);
+        S2 = mfma32x32x16(r1, b1, S2);
+        S = mfma32x32x16(r2, b2, S);
+        S2 = mfma32x32x16(r3, b3, S2);
+      }
+    }
+    // keep the score block in VGPRs (the softmax works on it with VALU ops)
+    asm volatile("" : "+v"(S), "+v"(S2));
+    const uint8_t* scl = st + LY::kScaleOff + 32 * hf;  // fp8 per-token scales of this lane's tokens
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = S[i];
+      if (FP8) x *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
+      S[i] = x + S2[i];  // bf16: odd k-steps; fp8: rope part
+    }
+    return S;
+  };
+
+  // online softmax of one tile (log2 units); lane holds 16 tokens of head h: element i is token
+  // 16 (i >> 3) + 8 hf + (i & 7) of the tile.  p_j = 2^(x_j * scale * log2e - m).  Writes the
+  // bf16 probabilities, the head's rescale factor and the wave's rescale flag into buffer `pb`.
+  // Branch-free (rows past nvalid are masked with selects; every lane stores), so that the
+  // compiler can interleave it with the value MFMAs of the previous tile.
+  float m_run = -INFINITY, l_run = 0.f;   // of head h (score phase)
+  auto softmax = [&](f32x16 S, int nvalid, const uint8_t* st, int pb) __attribute__((always_inline)) {
+    const int nv = nvalid - 8 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = (16 * (i >> 3) + (i & 7) < nv) ? S[i] : -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.sl2;
+    const bool need = mx > m_run + 8.0f;
+    const int any = __builtin_amdgcn_ballot_w64(need) != 0 ? 1 : 0;
+    const float m_new = need ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless raised (m_run = -inf: 0)
+    m_run = m_new;
+    l_run *= alpha;
+    alpha_s[pb][h] = alpha;        // lanes l and l ^ 32 hold the same head and store the same value
+    flags_s[pb][wave] = any;       // every lane stores the same value
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], a.sl2, -m_run));
+      l_run += S[i];
+    }
+    if (FP8) {
+      const uint8_t* scl = st + LY::kScaleOff + 32 * hf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
+    }
+    const u32x4 pb0 = {pack_bf16x2(S[0], S[1]), pack_bf16x2(S[2], S[3]), pack_bf16x2(S[4], S[5]),
+                       pack_bf16x2(S[6], S[7])};
+    const u32x4 pb1 = {pack_bf16x2(S[8], S[9]), pack_bf16x2(S[10], S[11]), pack_bf16x2(S[12], S[13]),
+                       pack_bf16x2(S[14], S[15])};
+    uint8_t* pw = pbuf[pb] + wave * 32 * kPbStride + pb_base;
+    *(u32x4*)(pw) = pb0;
+    *(u32x4*)(pw + 32) = pb1;
+  };
+
+  // acc[hb * CPW + j]: O^T rows (latent columns) 32 * (wave * CPW + j) .. +31, heads 32 hb .. +31
+  f32x16 acc[16];
+  // rescale the accumulator blocks of every head block whose running maximum rose in the tile
+  // that wrote buffer pb (in-place AGPR multiply, one register at a time)
+  auto read_flags = [&](int pb) __attribute__((always_inline)) -> u32x4 { return *(const u32x4*)flags_s[pb]; };
+  auto rescale_with = [&](const u32x4 fl, int pb) __attribute__((always_inline)) {
+    uint32_t fany = 0;
+#pragma unroll
+    for (int hb = 0; hb < NWAVE; ++hb) fany |= fl[hb];
+    if (__builtin_amdgcn_readfirstlane(fany) == 0) return;
+#pragma unroll
+    for (int hb = 0; hb < NWAVE; ++hb) {
+      if (__builtin_amdgcn_readfirstlane(fl[hb])) {
+        const float al = alpha_s[pb][hb * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float x = acc[hb * CPW + j][v];
+            float t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t) : "v"(al));
+            acc[hb * CPW + j][v] = x;
+          }
+        }
+      }
+    }
+  };  // one LDS read for the flags of every wave; usually none is set
+  auto rescale = [&](int pb) __attribute__((always_inline)) { rescale_with(read_flags(pb), pb); };
+
+  // value block: this wave's latent columns for all heads of the workgroup, from the tile in stage
+  // st and the probabilities in buffer pb:  acc[hb][j] (O^T) += C^T . P
+  auto value = [&](const uint8_t* st, int pb) __attribute__((always_inline)) {
+    auto val_op = [&](int cb, int ks) __attribute__((always_inline)) -> LatRaw {
+      if constexpr (!FP8) {
+        const uint8_t* p0 = st + val_base + 16 * kLatStride * ks + 64 * cb;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLatStride));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      } else {
+        const uint8_t* p0 = st + val_base + 8 * kLatStride * ks + 32 * cb;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(p0));
+        return __builtin_bit_cast(u32x2, v);
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pbv[NWAVE];
+#pragma unroll
+      for (int hb = 0; hb < NWAVE; ++hb) pbv[hb] = *(const u32x4*)(pbuf[pb] + hb * 32 * kPbStride + pb_base + 32 * ks);
+#pragma unroll
+      for (int j0 = 0; j0 < CPW; j0 += 2) {
+        const u32x4 av0 = widen(val_op(wave * CPW + j0, ks));
+        const u32x4 av1 = widen(val_op(wave * CPW + j0 + 1, ks));
+#pragma unroll
+        for (int hb = 0; hb < NWAVE; ++hb) {
+          acc[hb * CPW + j0] = mfma32x32x16(av0, pbv[hb], acc[hb * CPW + j0]);
+          acc[hb * CPW + j0 + 1] = mfma32x32x16(av1, pbv[hb], acc[hb * CPW + j0 + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
+  };
+
+  // ---------------------------------------------------------------- pipeline
+  // Tile it: wait for its loads, barrier (publishes the tile, the probabilities of tile it-1 and
+  // frees the stage of tile it-2), issue the loads of tile it+1 into that stage, then
+  //   score(it) ; value(it-1) ; softmax(it)
+  // in one basic block, so that the softmax of tile it runs under the value MFMAs of tile it-1.
+  // The first tile of a segment has no value step; the last one's value runs after the loop
+  // (behind one more barrier), before the segment's partial is written.
+  auto stage = [&](int i) __attribute__((always_inline)) -> const uint8_t* { return smem + (i % kNst) * LY::kStage; };
   issue(0);
-  if (ntiles > 1) issue(1);
+  // source of tile it + 1, located during the previous tile (tile indices past the end are
+  // clamped to the last tile: the lookup is then harmless and unused)
+  TileSrc nsrc = prep(min(1, ntiles - 1));
 
   int it = 0;
   int cb_seq = seq_of_tile(P, a.B, t_begin);
@@ -271,9 +505,9 @@ void k_partial_mfma(PartialArgs a) {
     while (t_begin + it >= P[cb_seq + 1]) ++cb_seq;
     const int b = __builtin_amdgcn_readfirstlane(cb_seq);
     const int it_end = min(ntiles, P[b + 1] - t_begin);
-    const int len_b = L[b];
+    const int len_b = load_uniform_i32(a.seq_lens + b);
+    const int tok_base = (t_begin - P[b]) * kTile;   // token index of tile 0 of this workgroup in b
 
-    u32x4 qf[QREG];
     {
       const uint16_t* qa = (const uint16_t*)a.q_abs + ((int64_t)b * H + h) * 512 + 8 * hf;
 #pragma unroll
@@ -291,210 +525,72 @@ void k_partial_mfma(PartialArgs a) {
         *(u32x4*)(qrs + wave * 4096 + 16 * (32 * c + (lane & 31))) = v;
       }
     }
-    // Complete the folded-query loads here, once per segment (this also waits for the tiles in
-    // flight), so that no wait on them is left inside the tile loop, where any vmcnt wait would
-    // also drain the tile DMA pipeline.
+    // Complete the folded-query loads (and the loads of tile it) here, once per segment, so that
+    // no wait on them is left inside the tile loop.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // acc[hb * CPW + j]: O^T rows (latent columns) 32 * (wave * CPW + j) .. +31, heads 32 hb .. +31
-    f32x16 acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;   // of head h (score phase)
+    m_run = -INFINITY;
+    l_run = 0.f;
 
-    for (; it < it_end; ++it) {
-      if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // first tile of the segment: score and softmax only
+    {
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());   // q_R / folded-query LDS writes done
       lds_barrier();
-      // spread the next tile's loads over the score k-steps (one wave per workgroup issues all
-      // 36 at once: spread, their addresses would not fit in its registers)
-      constexpr bool kSpread = NWAVE >= 2;
-      const bool pre = it + 2 < ntiles;
-      TileSrc nxt;
-      if (pre) {
-        if (kSpread) nxt = prep(it + 2);
-        else issue(it + 2);
-      }
-
-      const int nvalid = min(kTile, len_b - (t_begin + it - P[b]) * kTile);
-      const uint8_t* st = smem + (it % kNst) * LY::kStage;
-
-      // ---- score block of this wave's 32 heads: S^T[token rows][heads]
-      f32x16 S = {}, S2 = {};
-      // latent score operand: bf16 rows read as 16 bytes; fp8 rows read as 8 raw bytes and widened
-      // to bf16 just before the MFMA that consumes them (keeps prefetched operands small)
-      using LatRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
-      auto lat_op = [&](int s) -> LatRaw {
-        if constexpr (!FP8) return *(const u32x4*)(st + sc_base + 32 * s);
-        else return *(const u32x2*)(st + ((s & 1) ? sc_base_odd : sc_base) + 16 * s);
-      };
-      auto widen = [&](const LatRaw& r) -> u32x4 {
-        if constexpr (!FP8) return r;
-        else return fp8x8_to_bf16x8(r);
-      };
-      auto rope_op = [&](int q) -> u32x4 { return *(const u32x4*)(st + rope_base + 1024 * q); };
-      auto q_lds = [&](int s) -> u32x4 {
-        return *(const u32x4*)(qls + wave * (32 - QREG) * 1024 + qr_base + 1024 * (s - QREG));
-      };
-      LatRaw a0 = lat_op(0), a1 = lat_op(1);
-#pragma unroll
-      for (int s = 0; s < 32; s += 2) {
-        LatRaw n0 = a0, n1 = a1;
-        if (s + 2 < 32) {
-          n0 = lat_op(s + 2);
-          n1 = lat_op(s + 3);
-        }
-        asm volatile("" ::: "memory");
-        if (kSpread && pre && (s / 2) * LPT / 16 < (s / 2 + 1) * LPT / 16) {
-          uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
-          asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
-#pragma unroll
-          for (int k = (s / 2) * LPT / 16; k < (s / 2 + 1) * LPT / 16; ++k) job(nxt, k, vx0, vx1, vf0, vf1);
-        }
-        // two accumulators: consecutive MFMAs are independent (a dependent 32x32x16 chain issues
-        // at roughly 60% of the independent rate)
-        const u32x4 q0 = (s < QREG) ? qf[s < QREG ? s : 0] : q_lds(s);
-        const u32x4 q1 = (s + 1 < QREG) ? qf[s + 1 < QREG ? s + 1 : 0] : q_lds(s + 1);
-        S = mfma32x32x16(widen(a0), q0, S);
-        S2 = mfma32x32x16(widen(a1), q1, S2);
-        a0 = n0;
-        a1 = n1;
-      }
-      {
-        // rope k-steps: A = rope keys of the tile, B = q_R of the wave's heads (both LDS)
-        const uint8_t* qrow = qrs + wave * 4096 + qr_base;
-        const u32x4 b0 = *(const u32x4*)(qrow);
-        const u32x4 b1 = *(const u32x4*)(qrow + 1024);
-        const u32x4 b2 = *(const u32x4*)(qrow + 2048);
-        const u32x4 b3 = *(const u32x4*)(qrow + 3072);
-        const u32x4 r0 = rope_op(0), r1 = rope_op(1), r2 = rope_op(2), r3 = rope_op(3);
-        if (FP8) {
-          S += S2;  // latent part (scaled per token in the softmax); rope part accumulates in S2
-          S2 = f32x16{};
-          S2 = mfma32x32x16(r0, b0, S2);
-          S2 = mfma32x32x16(r1, b1, S2);
-          S2 = mfma32x32x16(r2, b2, S2);
-          S2 = mfma32x32x16(r3, b3, S2);
-        } else {
-          S = mfma32x32x16(r0, b0, S);
-          S2 = mfma32x32x16(r1, b1, S2);
-          S = mfma32x32x16(r2, b2, S);
-          S2 = mfma32x32x16(r3, b3, S2);
-        }
-      }
-      // keep the score block in VGPRs (the softmax works on it with VALU ops)
-      asm volatile("" : "+v"(S), "+v"(S2));
-
-      // ---- online softmax (log2 units); lane holds 16 tokens of head h
-      //      raw score x_j (unscaled); p_j = 2^(x_j * scale * log2e - m)
-      //      element i of the lane holds token 16 (i >> 3) + 8 hf + (i & 7) of the tile
-      float mx = -INFINITY;
-      const uint8_t* scl = st + LY::kScaleOff + 32 * hf;  // fp8 per-token scales of this lane's tokens
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = S[i];
-        if (FP8) x *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
-        S[i] = x + S2[i];  // bf16: odd k-steps; fp8: rope part
-      }
-      if (nvalid < kTile) {  // ragged last tile of a sequence: mask rows past its length
-        const int nv = nvalid - 8 * hf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (16 * (i >> 3) + (i & 7) >= nv) S[i] = -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.sl2;
-      const bool need = mx > m_run + 8.0f;
-      const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-      if (any) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        if (lane < 32) alpha_s[h] = alpha;
-      }
-      if (lane == 0) flags_s[wave] = any ? 1 : 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], a.sl2, -m_run));
-        l_run += S[i];
-      }
-      if (FP8) {
-        // re-read the per-token scales here instead of keeping 16 of them live across the softmax
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[i] *= *(const float*)(scl + 4 * (16 * (i >> 3) + (i & 7)));
-      }
-      {
-        const u32x4 pb0 = {pack_bf16x2(S[0], S[1]), pack_bf16x2(S[2], S[3]), pack_bf16x2(S[4], S[5]),
-                           pack_bf16x2(S[6], S[7])};
-        const u32x4 pb1 = {pack_bf16x2(S[8], S[9]), pack_bf16x2(S[10], S[11]), pack_bf16x2(S[12], S[13]),
-                           pack_bf16x2(S[14], S[15])};
-        uint8_t* pw = pbuf + wave * 32 * kPbStride + pb_base;
-        *(u32x4*)(pw) = pb0;
-        *(u32x4*)(pw + 32) = pb1;
-      }
-      // publish probabilities, rescale factors and flags of every wave's heads
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
-      lds_barrier();
-
-      // ---- value block: this wave's latent columns for all heads of the workgroup
-      //      acc[hb][j] (O^T, columns 32 (wave*CPW + j) .., heads 32 hb ..) += C^T . P
-#pragma unroll
-      for (int hb = 0; hb < NWAVE; ++hb) {
-        if (flags_s[hb]) {
-          const float al = alpha_s[hb * 32 + (lane & 31)];
-          // in-place AGPR rescale, one register at a time (keeps the accumulator in AGPRs)
-#pragma unroll
-          for (int j = 0; j < CPW; ++j) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float x = acc[hb * CPW + j][v];
-              float t;
-              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                           : "+a"(x), "=&v"(t) : "v"(al));
-              acc[hb * CPW + j][v] = x;
-            }
-          }
-        }
-      }
-      auto val_op = [&](int cb, int ks) -> LatRaw {
-        if constexpr (!FP8) {
-          const uint8_t* p0 = st + val_base + 16 * kLatStride * ks + 64 * cb;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLatStride));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          return u32x4{l2[0], l2[1], h2[0], h2[1]};
-        } else {
-          const uint8_t* p0 = st + val_base + 8 * kLatStride * ks + 32 * cb;
-          const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(p0));
-          return __builtin_bit_cast(u32x2, v);
-        }
-      };
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pbv[NWAVE];
-#pragma unroll
-        for (int hb = 0; hb < NWAVE; ++hb) pbv[hb] = *(const u32x4*)(pbuf + hb * 32 * kPbStride + pb_base + 32 * ks);
-#pragma unroll
-        for (int j0 = 0; j0 < CPW; j0 += 2) {
-          const u32x4 av0 = widen(val_op(wave * CPW + j0, ks));
-          const u32x4 av1 = widen(val_op(wave * CPW + j0 + 1, ks));
-#pragma unroll
-          for (int hb = 0; hb < NWAVE; ++hb) {
-            acc[hb * CPW + j0] = mfma32x32x16(av0, pbv[hb], acc[hb * CPW + j0]);
-            acc[hb * CPW + j0 + 1] = mfma32x32x16(av1, pbv[hb], acc[hb * CPW + j0 + 1]);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
+      if (it + 1 < ntiles) issue_src(nsrc);
+      const int nn = min(it + 2, ntiles - 1);
+      advance(nn);
+      nsrc = locate(nn);
+      const int nvalid = min(kTile, len_b - (tok_base + it * kTile));
+      const f32x16 S = score(stage(it), std::false_type{}, nsrc);
+      softmax(S, nvalid, stage(it), it & 1);
+      ++it;
     }
+    // steady tiles that have a next tile to load: its loads are spread over the score MFMAs
+    // (bf16; the fp8 variants issue them before the score, which keeps them free of spills)
+    const int it_dma_end = min(it_end, ntiles - 1);
+    for (; it < it_dma_end; ++it) {
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_imm0());   // tile it landed; this wave's probabilities written
+      lds_barrier();
+      // bf16: the flags are read here and acted on after the score MFMAs (the read's latency
+      // hides under them); fp8: rescale first (fewer live registers across the score)
+      u32x4 fl = {0u, 0u, 0u, 0u};
+      if constexpr (FP8) {
+        issue_src(nsrc);
+        rescale((it - 1) & 1);
+      } else {
+        fl = read_flags((it - 1) & 1);
+      }
+      const TileSrc cur = nsrc;
+      const int nn = min(it + 2, ntiles - 1);
+      advance(nn);
+      nsrc = locate(nn);
+      const int nvalid = min(kTile, len_b - (tok_base + it * kTile));
+      const f32x16 S = score(stage(it), std::integral_constant<bool, !FP8>{}, cur);
+      if constexpr (!FP8) rescale_with(fl, (it - 1) & 1);
+      value(stage(it - 1), (it - 1) & 1);
+      softmax(S, nvalid, stage(it), it & 1);
+    }
+    // the workgroup's last tile, if it is in this segment (nothing left to load)
+    if (it < it_end) {
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_imm0());
+      lds_barrier();
+      rescale((it - 1) & 1);
+      const int nvalid = min(kTile, len_b - (tok_base + it * kTile));
+      const f32x16 S = score(stage(it), std::false_type{}, nsrc);
+      value(stage(it - 1), (it - 1) & 1);
+      softmax(S, nvalid, stage(it), it & 1);
+      ++it;
+    }
+    // value of the segment's last tile (its probabilities are published by this barrier)
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
+    lds_barrier();
+    rescale((it - 1) & 1);
+    value(stage(it - 1), (it - 1) & 1);
 
     // ------------------------------------------------------------ segment partial -> slot w + b
     {
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-      const int64_t slot = (int64_t)(w + b) * H;
       // opaque copy of the lane id: keeps these addresses from being hoisted out of the segment
       // loop (where they would occupy registers for the whole tile loop)
       int ln = lane;
@@ -513,7 +609,7 @@ void k_partial_mfma(PartialArgs a) {
           }
         }
       }
-      if (ln < 32) *(f32x2*)(a.ws_ml + (slot + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};
+      if (ln < 32) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};
     }
   }
 }

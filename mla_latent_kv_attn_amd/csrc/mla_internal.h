@@ -136,12 +136,13 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 
 __device__ __forceinline__ int tiles_of(int len) { return (len + kTile - 1) / kTile; }
 
-// Builds P[0..B] (LDS) = prefix sums of tile counts, and L[0..B) = lengths. Ends with a barrier.
+// Builds P[0..B] (LDS) = prefix sums of tile counts, and L[0..B) = lengths (unless L is null).
+// Ends with a barrier.
 __device__ __forceinline__ void build_tile_prefix(const int32_t* __restrict__ lens, int B, int* P, int* L) {
   const int tid = threadIdx.x;
   for (int b = tid; b < B; b += blockDim.x) {
     int len = lens[b];
-    L[b] = len;
+    if (L) L[b] = len;
     P[b + 1] = tiles_of(len);
   }
   if (tid == 0) P[0] = 0;

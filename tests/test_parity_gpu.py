@@ -134,6 +134,9 @@ MINI = {
     "h64": (mini(2, name="mini-h64", B=2, H=64, n_max=130, len_lo=1, len_hi=130), [130, 40]),
     "h32": (mini(2, name="mini-h32", B=2, H=32, n_max=130, len_lo=1, len_hi=130), [77, 130]),
     "f32-var": (mini(1, name="mini-f32", B=4, n_max=100, len_lo=1, len_hi=100), [100, 1, 0, 33]),
+    "fp8-h32": (mini(5, name="mini-fp8-h32", B=3, H=32, n_max=200, len_lo=1, len_hi=200), [200, 33, 0]),
+    "fp8-h64": (mini(5, name="mini-fp8-h64", B=2, H=64, n_max=130, len_lo=1, len_hi=130), [1, 130]),
+    "paged-h64": (mini(4, name="mini-paged-h64", B=3, H=64, n_max=192, len_lo=1, len_hi=192), [192, 64, 65]),
 }
 
 
