@@ -103,6 +103,16 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* p) {
 }
 
 constexpr int lgkmcnt_imm0() { return 15 | (3 << 14) | (7 << 4); }
+
+// Score MFMAs with the accumulator in VGPRs (inline asm: the builtin would place it in AGPRs,
+// which the output accumulator fills, forcing copies).  Back-to-back MFMAs accumulating into the
+// same registers need no wait states; the caller adds the wait before VALU reads of the result.
+__device__ __forceinline__ void mfma_v_first(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
 // s_waitcnt immediate waiting for vmcnt == 0 and lgkmcnt == 0 (tile loads landed, own LDS writes done)
 constexpr int vm_lgkm_imm0() { return 7 << 4; }
 
@@ -332,8 +342,18 @@ void k_partial_mfma(PartialArgs a) {
       // at roughly 60% of the independent rate)
       const u32x4 q0 = (s < QREG) ? qf[s < QREG ? s : 0] : q_lds(s);
       const u32x4 q1 = (s + 1 < QREG) ? qf[s + 1 < QREG ? s + 1 : 0] : q_lds(s + 1);
-      S = mfma32x32x16(widen(a0), q0, S);
-      S2 = mfma32x32x16(widen(a1), q1, S2);
+      if constexpr (!FP8) {
+        if (s == 0) {
+          mfma_v_first(S, a0, q0);
+          mfma_v_first(S2, a1, q1);
+        } else {
+          mfma_v(S, a0, q0);
+          mfma_v(S2, a1, q1);
+        }
+      } else {
+        S = mfma32x32x16(widen(a0), q0, S);
+        S2 = mfma32x32x16(widen(a1), q1, S2);
+      }
       if constexpr (kJobs) {
         const int k0 = (s / 2) * LPT / 16, k1 = (s / 2 + 1) * LPT / 16;   // constants after unrolling
         if (k0 < k1) {
@@ -360,14 +380,21 @@ void k_partial_mfma(PartialArgs a) {
         S2 = mfma32x32x16(r2, b2, S2);
         S2 = mfma32x32x16(r3, b3, S2);
       } else {
-        S = mfma32x32x16(r0, b0, S);
-        S2 = mfma32x32x16(r1, b1, S2);
-        S = mfma32x32x16(r2, b2, S);
-        S2 = mfma32x32x16(r3, b3, S2);
+        mfma_v(S, r0, b0);
+        mfma_v(S2, r1, b1);
+        mfma_v(S, r2, b2);
+        mfma_v(S2, r3, b3);
       }
     }
-    // keep the score block in VGPRs (the softmax works on it with VALU ops)
-    asm volatile("" : "+v"(S), "+v"(S2));
+    if constexpr (!FP8) {
+      // VALU reads of an MFMA result need 12 wait states after the MFMA that wrote it (what the
+      // compiler itself inserts for this instruction); 16 here, tied to S and S2 so that no read
+      // of them can be scheduled above it
+      asm volatile("s_nop 15" : "+v"(S), "+v"(S2));
+    } else {
+      // keep the score block in VGPRs (the softmax works on it with VALU ops)
+      asm volatile("" : "+v"(S), "+v"(S2));
+    }
     const uint8_t* scl = st + LY::kScaleOff + 32 * hf;  // fp8 per-token scales of this lane's tokens
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
