@@ -4,9 +4,9 @@
 //   absorb:  q'[b,h,:]  = W_UK[h]^T q_C[b,h,:]   ([B x 128] . [128 x 512] per head)
 //   uv:      o[b,h,:]   = W_UV[h] o_lat[b,h,:]   ([B x 512] . [512 x 128] per head)
 //
-// ("Grouped-query and latent attention", section "The absorption trick".)  Both read their weight
-// once per launch for batches up to 128 (absorb) / 32 (uv) rows per workgroup; at B = 1 they are
-// bandwidth-bound streams over the 16.8 MB weight.
+// ("Grouped-query and latent attention", section "The absorption trick".)  The MFMA kernels read
+// the weight once per 128 (absorb) / 32 (uv) batch rows; for B <= 4 the streaming kernels below
+// read it once, as plain bandwidth-bound passes over the 16.8 MB weight.
 #include "mla_internal.h"
 
 namespace mla {
@@ -143,10 +143,11 @@ hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// uv.  Grid (H, 2 halves of the 128 output rows, ceil(B/32)), 128 threads.  Wave w computes
-// output rows i0 .. i0+31 (i0 = 64*half + 32w) for batch rows b0 .. b0+31.  Operand A = o_lat
-// rows (fp32, split into bf16 hi + bf16 lo so the product keeps ~16 mantissa bits of o_lat),
-// operand B = W_UV[h][i][k] rows straight from global memory (k contiguous).
+// uv.  Grid (H, ceil(B/32)), 256 threads.  The workgroup computes all 128 output rows of head h
+// for batch rows b0 .. b0+31: wave w takes output rows 32w .. 32w+31.  Operand A = o_lat rows,
+// fp32 split into bf16 hi + bf16 lo (the product keeps ~16 mantissa bits of o_lat); the split is
+// done once per workgroup into LDS (32 rows x 512 columns x 2 halves, 64 KiB), where every wave
+// reads it.  Operand B = W_UV[h][i][k] rows straight from global memory (k contiguous).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, u32x4& hi, u32x4& lo) {
   const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -158,35 +159,48 @@ __device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, 
   }
 }
 
-__global__ __launch_bounds__(128) void k_uv_bf16(const float* __restrict__ o_lat, const uint16_t* __restrict__ w,
+constexpr int kUvRow = 1024 + 16;   // LDS bytes per o_lat row and half (512 bf16 + pad)
+
+__global__ __launch_bounds__(256) void k_uv_bf16(const float* __restrict__ o_lat, const uint16_t* __restrict__ w,
                                                  float* __restrict__ out, int B, int H) {
-  const int h = blockIdx.x, ih = blockIdx.y, bz = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i0 = ih * 64 + wave * 32;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][32 * kUvRow];   // [hi/lo][row][k]
+  const int h = blockIdx.x, bz = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b0 = bz * 32;
-  const int brow = b0 + (lane & 31), kh = lane >> 5;
-  const bool bvalid = brow < B;
-  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh;
-  const float* xr = o_lat + ((int64_t)(bvalid ? brow : 0) * H + h) * 512 + 8 * kh;
-  f32x16 acc = {};
-#pragma unroll 8
-  for (int ks = 0; ks < 32; ++ks) {
-    const u32x4 bw = *(const u32x4*)(wr + 16 * ks);
+  // stage: thread t converts 8 consecutive columns (8 (t % 64) ..) of rows t / 64 + 4 j
+  for (int r = tid >> 6; r < 32; r += 4) {
+    const int b = b0 + r;
     float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (bvalid) {
-      x0 = *(const float4*)(xr + 16 * ks);
-      x1 = *(const float4*)(xr + 16 * ks + 4);
+    if (b < B) {
+      const float* src = o_lat + ((int64_t)b * H + h) * 512 + 8 * lane;
+      x0 = *(const float4*)src;
+      x1 = *(const float4*)(src + 4);
     }
     u32x4 hi, lo;
     split_hi_lo(x0, x1, hi, lo);
+    *(u32x4*)(xs[0] + r * kUvRow + 16 * lane) = hi;
+    *(u32x4*)(xs[1] + r * kUvRow + 16 * lane) = lo;
+  }
+  __syncthreads();
+  const int i0 = wave * 32;
+  const int kh = lane >> 5;
+  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh;
+  const uint8_t* ahi = xs[0] + (lane & 31) * kUvRow + 16 * kh;
+  const uint8_t* alo = xs[1] + (lane & 31) * kUvRow + 16 * kh;
+  f32x16 acc = {}, acc2 = {};
+#pragma unroll 8
+  for (int ks = 0; ks < 32; ++ks) {
+    const u32x4 bw = *(const u32x4*)(wr + 16 * ks);
+    const u32x4 hi = *(const u32x4*)(ahi + 32 * ks);
+    const u32x4 lo = *(const u32x4*)(alo + 32 * ks);
     acc = mfma32x32x16(hi, bw, acc);
-    acc = mfma32x32x16(lo, bw, acc);
+    acc2 = mfma32x32x16(lo, bw, acc2);
   }
   float* orow = out + (int64_t)h * 128 + i0 + (lane & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int b = b0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (b < B) orow[(int64_t)b * H * 128] = acc[v];
+    if (b < B) orow[(int64_t)b * H * 128] = acc[v] + acc2[v];
   }
 }
 
@@ -265,8 +279,8 @@ hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, 
       hipLaunchKernelGGL(k_uv_gemv<4>, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
     return hipGetLastError();
   }
-  dim3 grid(H, 2, (B + 31) / 32);
-  hipLaunchKernelGGL(k_uv_bf16, grid, dim3(128), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+  dim3 grid(H, (B + 31) / 32);
+  hipLaunchKernelGGL(k_uv_bf16, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
   return hipGetLastError();
 }
 

@@ -342,8 +342,94 @@ __global__ __launch_bounds__(1024) void k_combine_tiles(CombineArgs a) {
   }
 }
 
+// Combine for the tiled layout when the batch alone gives enough workgroups: grid (H/32, B), 256
+// threads; the workgroup merges all d_c/32 tiles of one 32-head block of one sequence, so the
+// (m, l) work is done once per head block.  Thread t owns element t of every tile (head t % 32):
+// d_c/32 float4 loads in flight per segment.  d_c must be 512.
+__global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
+  constexpr int NCB = 16;
+  __shared__ float red[8][32];
+  __shared__ float Ms[32], Lsum[32];
+  __shared__ float wts[kCombWB][32];
+  const int hb = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int H = a.H, d_c = a.d_c;
+  const int v = tid >> 6, l = tid & 63, r = l & 31;
+  const int hr = tid & 31, g = tid >> 5;
+  const int head = hb * 32 + r;
+  float* out = a.o_latent + ((int64_t)b * H + head) * d_c + 8 * v + 4 * (l >> 5);   // + 32 cb
+  const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
+  if (Pb1 == Pb) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) *(float4*)(out + 32 * cb) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse && tid < 32) a.lse[(int64_t)b * H + hb * 32 + tid] = -INFINITY;
+    return;
+  }
+  const int Wp = min(a.W, NT);
+  const int w0 = (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;   // owner of tile t: ceil((t+1)Wp/NT)-1
+  const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
+  const int nseg = w1 - w0 + 1;
+  const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + hb * 32) * 2);   // (s, head) at ml[s H + head]
+  float mloc = -INFINITY;
+  for (int s = g; s < nseg; s += 8) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
+  red[g][hr] = mloc;
+  __syncthreads();
+  if (tid < 32) {
+    float m = red[0][tid];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, red[i][tid]);
+    Ms[tid] = m;
+  }
+  __syncthreads();
+  {
+    const float M = Ms[hr];
+    float lloc = 0.f;
+    for (int s = g; s < nseg; s += 8) {
+      const float2 q = ml[(int64_t)s * H + hr];
+      const float f = exp2f(q.x - M);
+      if (s < kCombWB) wts[s][hr] = f;
+      lloc += f * q.y;
+    }
+    red[g][hr] = lloc;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float t = red[0][tid];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) t += red[i][tid];
+    Lsum[tid] = t;
+  }
+  __syncthreads();
+  const float M = Ms[r];
+  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
+  const float* src = a.ws_acc + (((int64_t)(w0 + b) * (H >> 5) + hb) * NCB) * 1024 + 4 * tid;   // + 1024 cb
+  float4 o[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nseg; ++s) {
+    float4 x[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) x[cb] = *(const float4*)(src + s * sstride + 1024 * cb);
+    const float f = s < kCombWB ? wts[s][r] : exp2f(ml[(int64_t)s * H + r].x - M);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      o[cb].x = fmaf(f, x[cb].x, o[cb].x);
+      o[cb].y = fmaf(f, x[cb].y, o[cb].y);
+      o[cb].z = fmaf(f, x[cb].z, o[cb].z);
+      o[cb].w = fmaf(f, x[cb].w, o[cb].w);
+    }
+  }
+  const float inv = 1.f / Lsum[r];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+    *(float4*)(out + 32 * cb) = make_float4(o[cb].x * inv, o[cb].y * inv, o[cb].z * inv, o[cb].w * inv);
+  if (a.lse && tid < 32)
+    a.lse[(int64_t)b * H + hb * 32 + tid] = (Ms[tid] + log2f(Lsum[tid])) * 0.69314718055994530942f;
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  if (ws_blocked(a.H, a.d_c))
+  if (ws_blocked(a.H, a.d_c) && a.d_c == 512 && (int64_t)(a.H / 32) * a.B >= 256)
+    hipLaunchKernelGGL(k_combine_heads, dim3(a.H / 32, a.B), dim3(256), 0, s, a);
+  else if (ws_blocked(a.H, a.d_c))
     hipLaunchKernelGGL(k_combine_tiles, dim3(a.H / 32, a.d_c / 32, a.B), dim3(1024), 0, s, a);
   else
     hipLaunchKernelGGL(k_combine_rows, dim3(a.H, a.B, (a.d_c + 127) / 128), dim3(256), 0, s, a);

@@ -253,3 +253,18 @@ def test_projections_batch_sweep(B):
     print(f"[parity] projections B={B}: q_abs {e_q:.3e} o {e_o:.3e}", flush=True)
     # q_abs is rounded once to bf16 (2^-9 relative); o is an fp32 product of exact inputs
     assert e_q <= 4e-3 and e_o <= 1e-4
+
+
+@pytest.mark.parametrize("H,B,splits", [(128, 64, 0), (128, 64, 200), (64, 128, 300)])
+def test_wide_batch_combine(H, B, splits):
+    """Batches wide enough (H/32 * B >= 256) for the combine pass to take one workgroup per
+    (32-head block, sequence): full comparison, with empty sequences and several segments per
+    sequence."""
+    wl = WORKLOADS[3].with_(name=f"wide-h{H}-b{B}", B=B, H=H, n_max=96, len_lo=0, len_hi=96)
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 97, size=B)
+    lens[:3] = [0, 1, 96]
+    inp = make_inputs(wl, lens=lens)
+    got = run_gpu(inp, num_splits=splits)
+    all_finite(got, inp)
+    compare(inp, got, oracle.decode(inp))
