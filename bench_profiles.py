@@ -69,6 +69,20 @@ def cmd_stats(a):
         lines.append(f"| {short} | {_col(r, 'Calls')} | {float(_col(r, 'AverageNs')) / 1e3:.2f} | "
                      f"{float(_col(r, 'MinNs')) / 1e3:.2f} | {float(_col(r, 'MaxNs')) / 1e3:.2f} | "
                      f"{float(_col(r, 'Percentage')):.1f} |")
+    if a.trace and bench:
+        # the bench's per-kernel timing loop is the last kernel_reps dispatches of each kernel
+        disp = {}
+        for r in _rows(a.trace):
+            name = _col(r, "Kernel_Name").split("(")[0].replace("void ", "")
+            disp.setdefault(name, []).append((int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp"))))
+        lines += ["", f"Average over the last {a.loop} dispatches of each kernel (the bench's events-timed loop; "
+                      "the table above also counts the graph-replayed steps):", ""]
+        for name, v in disp.items():
+            if not name.startswith("mla::"):
+                continue
+            v.sort()
+            tail = v[-a.loop:]
+            lines.append(f"    {name}: {statistics.mean(e - s_ for s_, e in tail) / 1e3:.2f} us")
     if bench:
         lines += ["", "bench.py line of the same run (HIP-event averages, us): " + json.dumps(bench["kernels_us"]),
                   f"ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
@@ -117,6 +131,8 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", default="")
     s.add_argument("--out", required=True)
+    s.add_argument("--trace", default=None, help="kernel_trace.csv of the same run")
+    s.add_argument("--loop", type=int, default=50, help="dispatches per kernel in the bench's timing loop")
     p = sub.add_parser("pmc")
     p.add_argument("--kernel", required=True)
     p.add_argument("--workload", required=True)
