@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of one absorbed MLA decode step on one MI355X.
 
-A step is the whole hot path on one batch: mla_absorb_q -> mla_decode_attn (partial pass +
-combine pass) -> mla_uv_out, over inputs already resident in HBM.  Prints one JSON line.
+A step is the whole hot path on one batch: mla_absorb_q -> mla_decode_partial ->
+mla_decode_combine_uv (the combine pass and mla_uv_out; one kernel at batch <= 4), over inputs
+already resident in HBM.  Prints one JSON line.
 
 Default workload: DeepSeek-V3-shape decode, B=1, H=128, d_c=512, d_R=64, N=4096 cached tokens,
 bf16 caches and weights (``--config 3/4/5`` selects the other synthetic workloads).
@@ -36,15 +37,23 @@ KERNEL_SOURCES = {
     "k_uv_bf16": "absorb_uv_mfma.hip",
     "k_uv_gemv": "absorb_uv_mfma.hip",
     "k_partial_mfma": "decode_partial_mfma.hip",
-    "k_combine_tiles": "decode_generic.hip",
+    "k_combine_rows": "decode_generic.hip",
+    "k_combine_heads": "decode_generic.hip",
+    "k_combine_uv": "absorb_uv_mfma.hip",
 }
+
+
+def fused_combine_uv(wl):
+    """Whether mla_decode_combine_uv runs as one kernel for this workload (the library's rule)."""
+    return wl.dtype != "f32" and wl.B <= 4 and wl.d_h == 128 and wl.d_c == 512
 
 
 def kernel_names(wl):
     """Kernel that each pass launches for this workload (the library's own dispatch rules)."""
     small = wl.B <= 4
     return {"absorb": "k_absorb_gemv" if small else "k_absorb_bf16", "partial": "k_partial_mfma",
-            "combine": "k_combine_tiles", "uv": "k_uv_gemv" if small else "k_uv_bf16"}
+            "combine": "k_combine_heads" if (wl.H // 32) * wl.B >= 256 else "k_combine_rows",
+            "uv": "k_uv_gemv" if small else "k_uv_bf16", "combine_uv": "k_combine_uv"}
 
 
 def parse():
@@ -83,14 +92,14 @@ def alg_bytes(wl, sum_len):
     partial = sum_len * per_tok + B * H * (d_c + d_R) * qb
     combine = B * H * d_c * 4 + B * H * 4
     uv = H * d_h * d_c * qb + B * H * d_c * 4 + B * H * d_h * 4
-    return {"absorb": absorb, "partial": partial, "combine": combine, "uv": uv}, per_tok
+    return {"absorb": absorb, "partial": partial, "combine": combine, "uv": uv, "combine_uv": combine + uv}, per_tok
 
 
 def alg_flops(wl, sum_len):
     B, H, d_h, d_c, d_R = wl.B, wl.H, wl.d_h, wl.d_c, wl.d_R
     return {"absorb": 2 * B * H * d_h * d_c,
             "partial": sum_len * (2 * H * (d_c + d_R) + 2 * H * d_c),
-            "combine": 0, "uv": 2 * B * H * d_h * d_c}
+            "combine": 0, "uv": 2 * B * H * d_h * d_c, "combine_uv": 2 * B * H * d_h * d_c}
 
 
 def cpu_baseline(inp, budget_s):
@@ -223,7 +232,7 @@ def main():
 
     # ---------------- per-kernel durations: HIP events around kernel_reps back-to-back launches of
     # one kernel (rotating input copies, so weights and caches stay cold), on the launch stream
-    names = ["absorb", "partial", "combine", "uv"]
+    names = ["absorb", "partial", "combine_uv"] if fused_combine_uv(wl) else ["absorb", "partial", "combine", "uv"]
     reps = args.kernel_reps
 
     def launch(name, r):
@@ -236,6 +245,9 @@ def main():
         elif name == "combine":
             ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent,
                                    step.lse, num_splits=args.num_splits, stream=stream)
+        elif name == "combine_uv":
+            ops.mla_decode_combine_uv(c["lens"], wl.n_max, step.workspace, c["W_UV"], step.o_latent, out=step.out,
+                                      lse=step.lse, num_splits=args.num_splits, stream=stream)
         else:
             ops.mla_uv_out(step.o_latent, c["W_UV"], out=step.out, stream=stream)
 
@@ -254,7 +266,7 @@ def main():
 
     ab, per_tok = alg_bytes(wl, sum_len)
     af = alg_flops(wl, sum_len)
-    step_bytes = sum(ab.values())
+    step_bytes = ab["absorb"] + ab["partial"] + ab["combine"] + ab["uv"]
     value = sum_len / (ms_per_step * 1e-3)
     dom = max(names, key=lambda n: kern_us[n])
     kname = kernel_names(wl)[dom]

@@ -186,6 +186,19 @@ int mla_decode_combine(const int32_t* seq_lens, int max_len, int B, int H, int d
                        const void* workspace, size_t workspace_bytes, float* o_latent, float* lse, void* stream);
 
 /*
+ * mla_decode_combine_uv -- the combine pass followed by mla_uv_out, as one call: the same
+ * arguments as mla_decode_combine (o_latent and lse are written exactly as there) plus W_UV
+ * [H, d_h, d_c] in w_dtype and out [B, H, d_h] float32 (written), with the semantics of
+ * mla_uv_out.  For a bf16 W_UV with d_h == 128, d_c == 512 and B <= 4 it is one kernel that
+ * starts streaming W_UV while it merges the partials (at small batch both passes are
+ * latency-bound); otherwise it launches the two passes.  Errors as for mla_decode_combine and
+ * mla_uv_out; nothing is launched when validation fails.
+ */
+int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
+                          const void* workspace, size_t workspace_bytes, const void* W_UV, int w_dtype, int d_h,
+                          float* out, float* o_latent, float* lse, void* stream);
+
+/*
  * mla_uv_out -- apply W_UV once to the weighted latent sum ("Grouped-query and
  * latent attention", section "The absorption trick": sum_j a_j W_UV c_j =
  * W_UV sum_j a_j c_j).

@@ -268,6 +268,185 @@ __global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat
   if ((lane & ((64 >> LK) - 1)) == 0 && b < B) out[((int64_t)b * H + h) * 128 + i0 + r] = t;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Combine + uv in one pass, small batch (B <= 4, d_h = 128, d_c = 512, row-major workspace).
+// Grid (H), 1024 threads (16 waves); the workgroup owns head h:
+//   1. wave w starts the loads of W_UV[h] rows 8w .. 8w+7 (lane l: columns 8l .. 8l+7) right
+//      after those of the first sequence's partials, so the weight stream overlaps step 2;
+//   2. per sequence b: the log-sum-exp merge of the segments' (m, l) and partial rows of head h
+//      into o_lat[b,h]: eight groups of 128 threads (one float4 column each) take every eighth
+//      segment, their first eight loads issued before the (m, l) reduction, and are summed
+//      through LDS; o_lat is kept in LDS and also written to o_latent (and lse);
+//   3. out[b,h,i] = W_UV[h][i] . o_lat[b,h] with the halving exchange of k_uv_gemv.
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(1024) void k_combine_uv(CombineArgs a, const uint16_t* __restrict__ w,
+                                                     float* __restrict__ out) {
+  constexpr int kW = 1024;   // segment weights kept in LDS
+  __shared__ __attribute__((aligned(16))) float ol[NB][512];
+  __shared__ float4 part[7][128];
+  __shared__ float wts[kW];
+  __shared__ float rr[16];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H;
+  // weight rows of this wave (8 rows x 16 B per lane), loaded after the first sequence's partials:
+  // loads complete in issue order, and the partials are needed first
+  u32x4 wv[8];
+  const int NT = a.ws_prefix[a.B];
+  const int c4 = tid & 127, sg = tid >> 7;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= a.B) break;
+    const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1];
+    float* orow = a.o_latent + ((int64_t)b * H + h) * 512;
+    const bool empty = Pb1 == Pb;
+    const int Wp = max(1, min(a.W, NT));
+    const int w0 = empty ? 0 : (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;   // owner of tile t: ceil((t+1)Wp/NT)-1
+    const int w1 = empty ? -1 : (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
+    const int nseg = w1 - w0 + 1;
+    const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml[s H]
+    const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 4 * c4;   // + s H 512
+    const int64_t sstride = (int64_t)H * 512;
+    // the partial rows of the first 64 segments do not depend on the weights: start their loads
+    // before the (m, l) reduction, so that both round trips overlap
+    const float2 q0 = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
+    float4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int su = sg + 8 * u;
+      x[u] = su < nseg ? *(const float4*)(src + su * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (b == 0) {
+      const uint16_t* wp = w + ((int64_t)h * 128 + wave * 8) * 512 + 8 * lane;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) wv[r] = *(const u32x4*)(wp + r * 512);
+    }
+    if (empty) {
+      if (sg == 0) {
+        *(float4*)&ol[b][4 * c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4*)(orow + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
+      continue;
+    }
+    float mloc = q0.x;
+    for (int s = tid + 1024; s < nseg; s += 1024) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, d, 64));
+    if (lane == 0) rr[wave] = mloc;
+    __syncthreads();
+    float M = rr[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) M = fmaxf(M, rr[i]);
+    __syncthreads();
+    float lloc = 0.f;
+    if (tid < nseg) {
+      const float f = exp2f(q0.x - M);
+      wts[tid] = f;
+      lloc = f * q0.y;
+    }
+    for (int s = tid + 1024; s < nseg; s += 1024) {
+      const float2 q = ml[(int64_t)s * H];
+      lloc += exp2f(q.x - M) * q.y;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) lloc += __shfl_xor(lloc, d, 64);
+    if (lane == 0) rr[wave] = lloc;
+    __syncthreads();
+    float Ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ls += rr[i];
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int su = sg + 8 * u;
+      const float f = su < nseg ? wts[su] : 0.f;
+      o.x = fmaf(f, x[u].x, o.x);
+      o.y = fmaf(f, x[u].y, o.y);
+      o.z = fmaf(f, x[u].z, o.z);
+      o.w = fmaf(f, x[u].w, o.w);
+    }
+    for (int s = sg + 64; s < nseg; s += 8) {
+      const float4 xs = *(const float4*)(src + s * sstride);
+      const float f = s < kW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M);
+      o.x = fmaf(f, xs.x, o.x);
+      o.y = fmaf(f, xs.y, o.y);
+      o.z = fmaf(f, xs.z, o.z);
+      o.w = fmaf(f, xs.w, o.w);
+    }
+    if (sg > 0) part[sg - 1][c4] = o;
+    __syncthreads();
+    if (sg == 0) {
+#pragma unroll
+      for (int g = 0; g < 7; ++g) {
+        const float4 u = part[g][c4];
+        o.x += u.x;
+        o.y += u.y;
+        o.z += u.z;
+        o.w += u.w;
+      }
+      const float inv = 1.f / Ls;
+      const float4 r = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      *(float4*)&ol[b][4 * c4] = r;
+      *(float4*)(orow + 4 * c4) = r;
+    }
+    if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
+    __syncthreads();   // part / rr / wts are reused by the next sequence
+  }
+  __syncthreads();
+  // 3. out[b, h, 8 wave + r] for r in 0..7
+  float x[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float4 x0 = *(const float4*)&ol[b][8 * lane], x1 = *(const float4*)&ol[b][8 * lane + 4];
+    x[b][0] = x0.x; x[b][1] = x0.y; x[b][2] = x0.z; x[b][3] = x0.w;
+    x[b][4] = x1.x; x[b][5] = x1.y; x[b][6] = x1.z; x[b][7] = x1.w;
+  }
+  constexpr int K = NB * 8;
+  constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : 5;
+  float v[K];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        acc = fmaf(x[b][2 * c2], __uint_as_float(wv[r][c2] << 16), acc);
+        acc = fmaf(x[b][2 * c2 + 1], __uint_as_float(wv[r][c2] & 0xffff0000u), acc);
+      }
+      v[b * 8 + r] = acc;
+    }
+#pragma unroll
+  for (int step = 0; step < LK; ++step) {
+    const int d = 32 >> step;
+    const int half = K >> (step + 1);
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? v[i] : v[i + half];
+      const float keep = upper ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, d, 64);
+    }
+  }
+  float t = v[0];
+#pragma unroll
+  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+  const int idx = (lane >> (6 - LK)) & (K - 1);
+  const int b = idx >> 3, r = idx & 7;
+  if ((lane & ((64 >> LK) - 1)) == 0 && b < a.B) out[((int64_t)b * H + h) * 128 + wave * 8 + r] = t;
+}
+
+hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s) {
+  if (a.B == 1)
+    hipLaunchKernelGGL(k_combine_uv<1>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+  else if (a.B == 2)
+    hipLaunchKernelGGL(k_combine_uv<2>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+  else
+    hipLaunchKernelGGL(k_combine_uv<4>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s) {
   if (B <= 4) {
     const dim3 grid(H, 4);

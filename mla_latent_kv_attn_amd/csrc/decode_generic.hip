@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = tid + i * 256;
-        if (k < d_c) a.ws_acc[ws_acc_index(slot, h, k, H, d_c)] = acc[i];
+        if (k < d_c) a.ws_acc[o * d_c + k] = acc[i];
       }
       if (tid == 0) {
         a.ws_ml[o * 2 + 0] = m;
@@ -238,129 +238,27 @@ __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
   if (a.lse && tid == 0 && cq == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
 }
 
-// Combine for the tiled acc layout (H % 32 == 0, d_c % 32 == 0).  Grid (H/32, d_c/32, B), 1024
-// threads; the workgroup merges one 32-head x 32-column tile.  Its four groups of 256 threads take
-// every fourth segment; thread 64 v + l of a group reads float4 (v, l) of the tile (4 KiB
-// contiguous per segment), eight segments in flight, and the groups are summed through LDS.
-// (m, l) of the 32 heads: thread t takes head t % 32 and segments t / 32 + 32 i.
 constexpr int kCombWB = 128;   // segments whose weights are kept in LDS (the rest are recomputed)
 
-__global__ __launch_bounds__(1024) void k_combine_tiles(CombineArgs a) {
-  __shared__ float red[32][32];
-  __shared__ float Ms[32], Lsum[32];
-  __shared__ float wts[kCombWB][32];
-  __shared__ float4 part[3][256];
-  const int hb = blockIdx.x, cb = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int H = a.H, d_c = a.d_c;
-  const int grp = tid >> 8, t8 = tid & 255;
-  const int v = t8 >> 6, l = t8 & 63, r = l & 31;               // accumulator element (v, l): head r
-  const int hr = tid & 31, g = tid >> 5;                         // (m, l) phase: head hr, group g
-  const int head = hb * 32 + r;
-  const int col = cb * 32 + 8 * v + 4 * (l >> 5);
-  float* out = a.o_latent + ((int64_t)b * H + head) * d_c + col;
-  const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
-  if (Pb1 == Pb) {
-    if (grp == 0) *(float4*)out = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.lse && cb == 0 && tid < 32) a.lse[(int64_t)b * H + hb * 32 + tid] = -INFINITY;
-    return;
-  }
-  const int Wp = min(a.W, NT);
-  const int w0 = (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;   // owner of tile t: ceil((t+1)Wp/NT)-1
-  const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
-  const int nseg = w1 - w0 + 1;
-  const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + hb * 32) * 2);   // (s, head) at ml[s H + head]
-  float mloc = -INFINITY;
-  for (int s = g; s < nseg; s += 32) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
-  red[g][hr] = mloc;
-  __syncthreads();
-  if (tid < 32) {
-    float m = red[0][tid];
-    for (int i = 1; i < 32; ++i) m = fmaxf(m, red[i][tid]);
-    Ms[tid] = m;
-  }
-  __syncthreads();
-  {
-    const float M = Ms[hr];
-    float lloc = 0.f;
-    for (int s = g; s < nseg; s += 32) {
-      const float2 q = ml[(int64_t)s * H + hr];
-      const float f = exp2f(q.x - M);
-      if (s < kCombWB) wts[s][hr] = f;
-      lloc += f * q.y;
-    }
-    red[g][hr] = lloc;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    float t = red[0][tid];
-    for (int i = 1; i < 32; ++i) t += red[i][tid];
-    Lsum[tid] = t;
-  }
-  __syncthreads();
-  const float M = Ms[r];
-  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
-  const float* src = a.ws_acc + (((int64_t)(w0 + b) * (H >> 5) + hb) * (d_c >> 5) + cb) * 1024 + 256 * v + 4 * l;
-  auto weight = [&](int s) -> float { return s < kCombWB ? wts[s][r] : exp2f(ml[(int64_t)s * H + r].x - M); };
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = grp;
-  for (; s + 28 < nseg; s += 32) {
-    float4 x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = *(const float4*)(src + (s + 4 * u) * sstride);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float f = weight(s + 4 * u);
-      o.x = fmaf(f, x[u].x, o.x);
-      o.y = fmaf(f, x[u].y, o.y);
-      o.z = fmaf(f, x[u].z, o.z);
-      o.w = fmaf(f, x[u].w, o.w);
-    }
-  }
-  for (; s < nseg; s += 4) {
-    const float4 x = *(const float4*)(src + s * sstride);
-    const float f = weight(s);
-    o.x = fmaf(f, x.x, o.x);
-    o.y = fmaf(f, x.y, o.y);
-    o.z = fmaf(f, x.z, o.z);
-    o.w = fmaf(f, x.w, o.w);
-  }
-  if (grp > 0) part[grp - 1][t8] = o;
-  __syncthreads();
-  if (grp == 0) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const float4 u = part[i][t8];
-      o.x += u.x;
-      o.y += u.y;
-      o.z += u.z;
-      o.w += u.w;
-    }
-    const float inv = 1.f / Lsum[r];
-    *(float4*)out = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    if (a.lse && cb == 0 && tid < 32)
-      a.lse[(int64_t)b * H + hb * 32 + tid] = (Ms[tid] + log2f(Lsum[tid])) * 0.69314718055994530942f;
-  }
-}
-
-// Combine for the tiled layout when the batch alone gives enough workgroups: grid (H/32, B), 256
-// threads; the workgroup merges all d_c/32 tiles of one 32-head block of one sequence, so the
-// (m, l) work is done once per head block.  Thread t owns element t of every tile (head t % 32):
-// d_c/32 float4 loads in flight per segment.  d_c must be 512.
+// Combine for batches wide enough to fill the chip with one workgroup per (32-head block,
+// sequence): grid (H/32, B), 256 threads.  The (m, l) reduction is done once per head block; the
+// block's 32 partial rows are 64 KiB contiguous per segment, which thread t reads as float4
+// t + 256 i (i = 0..15: head 2i + t / 128, columns 4 (t % 128) ..), sixteen loads in flight.
+// d_c must be 512.
 __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
-  constexpr int NCB = 16;
+  constexpr int NI = 16;
   __shared__ float red[8][32];
   __shared__ float Ms[32], Lsum[32];
   __shared__ float wts[kCombWB][32];
   const int hb = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = a.H, d_c = a.d_c;
-  const int v = tid >> 6, l = tid & 63, r = l & 31;
-  const int hr = tid & 31, g = tid >> 5;
-  const int head = hb * 32 + r;
-  float* out = a.o_latent + ((int64_t)b * H + head) * d_c + 8 * v + 4 * (l >> 5);   // + 32 cb
+  const int hr = tid & 31, g = tid >> 5;                       // (m, l) phase: head hr, group g
+  const int c4 = tid & 127, r0 = tid >> 7;                     // accumulate phase: heads r0 + 2i
+  float* out = a.o_latent + ((int64_t)b * H + hb * 32) * d_c + 4 * c4;   // + (r0 + 2i) d_c
   const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
   if (Pb1 == Pb) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) *(float4*)(out + 32 * cb) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < NI; ++i) *(float4*)(out + (r0 + 2 * i) * d_c) = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.lse && tid < 32) a.lse[(int64_t)b * H + hb * 32 + tid] = -INFINITY;
     return;
   }
@@ -369,6 +267,12 @@ __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
   const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
   const int nseg = w1 - w0 + 1;
   const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + hb * 32) * 2);   // (s, head) at ml[s H + head]
+  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
+  const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + hb * 32) * d_c + 4 * c4;   // + (r0 + 2i) d_c + s sstride
+  // the first segment's rows do not depend on the weights: load them during the (m, l) reduction
+  float4 x0[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) x0[i] = *(const float4*)(src + (r0 + 2 * i) * d_c);
   float mloc = -INFINITY;
   for (int s = g; s < nseg; s += 8) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
   red[g][hr] = mloc;
@@ -399,38 +303,38 @@ __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
     Lsum[tid] = t;
   }
   __syncthreads();
-  const float M = Ms[r];
-  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
-  const float* src = a.ws_acc + (((int64_t)(w0 + b) * (H >> 5) + hb) * NCB) * 1024 + 4 * tid;   // + 1024 cb
-  float4 o[NCB];
+  float4 o[NI];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) o[cb] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nseg; ++s) {
-    float4 x[NCB];
+  for (int i = 0; i < NI; ++i) {
+    const float f = wts[0][r0 + 2 * i];
+    o[i] = make_float4(f * x0[i].x, f * x0[i].y, f * x0[i].z, f * x0[i].w);
+  }
+  for (int s = 1; s < nseg; ++s) {
+    float4 x[NI];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) x[cb] = *(const float4*)(src + s * sstride + 1024 * cb);
-    const float f = s < kCombWB ? wts[s][r] : exp2f(ml[(int64_t)s * H + r].x - M);
+    for (int i = 0; i < NI; ++i) x[i] = *(const float4*)(src + s * sstride + (r0 + 2 * i) * d_c);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      o[cb].x = fmaf(f, x[cb].x, o[cb].x);
-      o[cb].y = fmaf(f, x[cb].y, o[cb].y);
-      o[cb].z = fmaf(f, x[cb].z, o[cb].z);
-      o[cb].w = fmaf(f, x[cb].w, o[cb].w);
+    for (int i = 0; i < NI; ++i) {
+      const int r = r0 + 2 * i;
+      const float f = s < kCombWB ? wts[s][r] : exp2f(ml[(int64_t)s * H + r].x - Ms[r]);
+      o[i].x = fmaf(f, x[i].x, o[i].x);
+      o[i].y = fmaf(f, x[i].y, o[i].y);
+      o[i].z = fmaf(f, x[i].z, o[i].z);
+      o[i].w = fmaf(f, x[i].w, o[i].w);
     }
   }
-  const float inv = 1.f / Lsum[r];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-    *(float4*)(out + 32 * cb) = make_float4(o[cb].x * inv, o[cb].y * inv, o[cb].z * inv, o[cb].w * inv);
+  for (int i = 0; i < NI; ++i) {
+    const float inv = 1.f / Lsum[r0 + 2 * i];
+    *(float4*)(out + (r0 + 2 * i) * d_c) = make_float4(o[i].x * inv, o[i].y * inv, o[i].z * inv, o[i].w * inv);
+  }
   if (a.lse && tid < 32)
     a.lse[(int64_t)b * H + hb * 32 + tid] = (Ms[tid] + log2f(Lsum[tid])) * 0.69314718055994530942f;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  if (ws_blocked(a.H, a.d_c) && a.d_c == 512 && (int64_t)(a.H / 32) * a.B >= 256)
+  if (a.H % 32 == 0 && a.d_c == 512 && (int64_t)(a.H / 32) * a.B >= 256)
     hipLaunchKernelGGL(k_combine_heads, dim3(a.H / 32, a.B), dim3(256), 0, s, a);
-  else if (ws_blocked(a.H, a.d_c))
-    hipLaunchKernelGGL(k_combine_tiles, dim3(a.H / 32, a.d_c / 32, a.B), dim3(1024), 0, s, a);
   else
     hipLaunchKernelGGL(k_combine_rows, dim3(a.H, a.B, (a.d_c + 127) / 128), dim3(256), 0, s, a);
   return hipGetLastError();

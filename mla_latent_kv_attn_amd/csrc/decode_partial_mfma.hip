@@ -622,18 +622,27 @@ void k_partial_mfma(PartialArgs a) {
       // loop (where they would occupy registers for the whole tile loop)
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      // tiled workspace layout: each accumulator register block is one 4 KiB tile (32 heads x
-      // 32 columns) stored as-is, one contiguous KiB per store instruction
+      // Row-major workspace: each 32x32 accumulator block goes through this wave's part of the
+      // (now idle) probability buffers, 144-byte rows, and leaves as 8 full 128-byte row
+      // segments per store instruction.  Every wave has finished reading the probabilities once
+      // it passes this barrier.
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
+      lds_barrier();
+      uint8_t* tb = &pbuf[0][0] + wave * 5120;
+      const int trow = ln >> 3, tchunk = ln & 7;
 #pragma unroll
       for (int hb = 0; hb < NWAVE; ++hb) {
-        float* dst = a.ws_acc + ((int64_t)(w + b) * NWAVE + hb) * 16 * 1024 + wave * CPW * 1024 + 4 * ln;
+        float* dst = a.ws_acc + ((int64_t)(w + b) * H + hb * 32 + trow) * 512 + 32 * wave * CPW + 4 * tchunk;
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
+          const f32x16& A = acc[hb * CPW + j];
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const f32x16& A = acc[hb * CPW + j];
-            *(f32x4*)(dst + 1024 * j + 256 * v4) = f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
-          }
+          for (int v4 = 0; v4 < 4; ++v4)
+            *(f32x4*)(tb + (ln & 31) * 144 + (8 * v4 + 4 * (ln >> 5)) * 4) =
+                f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(dst + (8 * q) * 512 + 32 * j) = *(const f32x4*)(tb + (8 * q + trow) * 144 + 16 * tchunk);
         }
       }
       if (ln < 32) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};

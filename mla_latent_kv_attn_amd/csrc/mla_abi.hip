@@ -249,4 +249,21 @@ int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out,
   return MLA_ERR_UNSUPPORTED;
 }
 
+int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
+                          const void* workspace, size_t workspace_bytes, const void* W_UV, int w_dtype, int d_h,
+                          float* out, float* o_latent, float* lse, void* stream) {
+  mla::CombineArgs ca;
+  int st = prepare_combine(seq_lens, max_len, B, H, d_c, num_splits, workspace, workspace_bytes, o_latent, lse, &ca);
+  if (st != MLA_OK) return st;
+  if (d_h < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(w_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!W_UV || !out) return MLA_ERR_NULL;
+  if (w_dtype == MLA_BF16 && d_h == 128 && d_c == 512 && B <= 4 && aligned16(W_UV))
+    return hip_status(mla::launch_combine_uv(ca, W_UV, out, (hipStream_t)stream));
+  st = hip_status(mla::launch_combine(ca, (hipStream_t)stream));
+  if (st != MLA_OK) return st;
+  return mla_uv_out(o_latent, W_UV, w_dtype, out, B, H, d_h, d_c, stream);
+}
+
 }  // extern "C"

@@ -51,20 +51,9 @@ struct CombineArgs {
 };
 
 // workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, each
-// 256-byte aligned.
-//
-// Inside the acc block a slot holds H x d_c floats.  When H % 32 == 0 and d_c % 32 == 0 they are
-// stored in 4 KiB tiles of 32 heads x 32 latent columns, in the order in which the partial pass's
-// MFMA accumulators hold them: tile (hb, cb) starts at float ((slot * H/32 + hb) * d_c/32 + cb) *
-// 1024, and element (head 32 hb + r, column 32 cb + c) sits at 256 (c / 8) + 4 (r + 32 ((c % 8) / 4))
-// + c % 4 inside it.  Every store of the partial pass then writes 1 KiB of contiguous memory.
-// Other shapes use row-major [slot][H][d_c].
-__host__ __device__ inline bool ws_blocked(int H, int d_c) { return H % 32 == 0 && d_c % 32 == 0; }
-__host__ __device__ inline int64_t ws_acc_index(int64_t slot, int h, int k, int H, int d_c) {
-  if (!ws_blocked(H, d_c)) return (slot * H + h) * d_c + k;
-  const int hb = h >> 5, r = h & 31, cb = k >> 5, c = k & 31;
-  return ((slot * (H >> 5) + hb) * (d_c >> 5) + cb) * 1024 + 256 * (c >> 3) + 4 * (r + 32 * ((c & 7) >> 2)) + (c & 3);
-}
+// 256-byte aligned.  A slot of the acc block holds H x d_c floats, row-major [slot][H][d_c]: the
+// partial pass writes whole 128-byte lines of a head's row, and a head's partial is contiguous
+// for the combine.
 inline size_t ws_slots(int W, int B) { return (size_t)W + (size_t)B - 1; }
 inline size_t ws_acc_bytes(int W, int B, int H, int d_c) {
   size_t b = ws_slots(W, B) * (size_t)H * (size_t)d_c * sizeof(float);
@@ -91,6 +80,7 @@ hipError_t launch_uv_f32w(const float* o_lat, const float* w, float* out, int B,
 hipError_t launch_uv_bf16w_generic(const float* o_lat, const void* w, float* out, int B, int H, int d_h,
                                    int d_c, hipStream_t s);
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s);
+hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s);
 
 }  // namespace mla
 

@@ -177,6 +177,24 @@ def mla_decode_combine(seq_lens, max_len: int, B: int, H: int, d_c: int, workspa
         o_latent.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream, o_latent)))
 
 
+def mla_decode_combine_uv(seq_lens, max_len: int, workspace, W_UV: torch.Tensor, o_latent: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, lse=None, num_splits: int = 0, stream=None):
+    """Combine pass + W_UV in one call: workspace partials -> o_latent [B,H,d_c] (and lse [B,H]),
+    then out[b,h] = W_UV[h] o_latent[b,h] ([B,H,d_h] float32)."""
+    _dev(seq_lens, workspace, W_UV, o_latent, out, lse)
+    B, H, d_c = o_latent.shape
+    d_h = W_UV.shape[1]
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=o_latent.device)
+    if not (W_UV.is_contiguous() and o_latent.is_contiguous() and out.is_contiguous()):
+        raise ValueError("W_UV, o_latent and out must be contiguous")
+    check("mla_decode_combine_uv", _lib.lib().mla_decode_combine_uv(
+        seq_lens.data_ptr(), int(max_len), B, H, d_c, int(num_splits), workspace.data_ptr(), workspace.numel(),
+        W_UV.data_ptr(), dtype_code(W_UV), d_h, out.data_ptr(), o_latent.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(stream, o_latent)))
+    return out
+
+
 def mla_uv_out(o_latent: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
     """out[b,h] = W_UV[h] o_latent[b,h].  o_latent [B,H,d_c] float32, W_UV [H,d_h,d_c]; out [B,H,d_h] float32."""
     _dev(o_latent, W_UV, out)

@@ -1,6 +1,7 @@
-"""One full absorbed decode step over preallocated buffers: mla_absorb_q -> mla_decode_attn ->
-mla_uv_out, all on one stream.  Buffers are allocated once (torch device memory) and reused, so a
-step issues four kernel launches and nothing else."""
+"""One full absorbed decode step over preallocated buffers, all on one stream:
+mla_absorb_q -> mla_decode_partial -> mla_decode_combine_uv (the combine pass and mla_uv_out; one
+kernel at batch <= 4, two otherwise).  Buffers are allocated once (torch device memory) and
+reused, so a step is three or four kernel launches and nothing else."""
 from __future__ import annotations
 
 import math
@@ -25,8 +26,8 @@ class DecodeStep:
 
     def __call__(self, q_C, q_R, W_UK, W_UV, cache: "ops.Cache", seq_lens, stream=None):
         ops.mla_absorb_q(q_C, W_UK, out=self.q_abs, stream=stream)
-        ops.mla_decode_attn(self.q_abs, q_R, cache, seq_lens, self.max_len, scale=self.scale,
-                            num_splits=self.num_splits, workspace=self.workspace, o_latent=self.o_latent,
-                            lse=self.lse, stream=stream)
-        ops.mla_uv_out(self.o_latent, W_UV, out=self.out, stream=stream)
+        ops.mla_decode_partial(self.q_abs, q_R, cache, seq_lens, self.max_len, self.scale, self.workspace,
+                               num_splits=self.num_splits, stream=stream)
+        ops.mla_decode_combine_uv(seq_lens, self.max_len, self.workspace, W_UV, self.o_latent, out=self.out,
+                                  lse=self.lse, num_splits=self.num_splits, stream=stream)
         return self.out

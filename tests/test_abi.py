@@ -133,3 +133,24 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     with pytest.raises(L.MlaLibraryError):
         L.lib()
 
+
+def test_combine_uv_validation(lib):
+    f = lib.mla_decode_combine_uv
+    need = lib.mla_decode_workspace_bytes(1, 128, 512, 4096, 0)
+    args = dict(lens=FAKE, max_len=4096, B=1, H=128, d_c=512, splits=0, ws=FAKE, ws_bytes=need, w=FAKE,
+                w_dtype=L.MLA_BF16, d_h=128, out=FAKE, o_lat=FAKE, lse=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["lens"], a["max_len"], a["B"], a["H"], a["d_c"], a["splits"], a["ws"], a["ws_bytes"], a["w"],
+                 a["w_dtype"], a["d_h"], a["out"], a["o_lat"], a["lse"], None)
+    assert call(B=-1) == L.MLA_ERR_SHAPE
+    assert call(d_h=0) == L.MLA_ERR_SHAPE
+    assert call(w_dtype=9) == L.MLA_ERR_DTYPE
+    assert call(ws=None) == L.MLA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == L.MLA_ERR_WORKSPACE
+    assert call(o_lat=None) == L.MLA_ERR_NULL
+    assert call(w=None) == L.MLA_ERR_NULL
+    assert call(out=None) == L.MLA_ERR_NULL
+    assert call(o_lat=FAKE + 4) == L.MLA_ERR_UNSUPPORTED
+    assert call(B=0) == L.MLA_OK

@@ -268,3 +268,38 @@ def test_wide_batch_combine(H, B, splits):
     got = run_gpu(inp, num_splits=splits)
     all_finite(got, inp)
     compare(inp, got, oracle.decode(inp))
+
+
+def run_step(inp, num_splits=0):
+    """The whole step through DecodeStep: absorb -> partial -> combine + W_UV (one fused kernel at
+    batch <= 4 with bf16 weights, otherwise the two passes)."""
+    from mla_latent_kv_attn_amd.step import DecodeStep
+    print(f"[gpu] step {inp.wl.name} B={inp.wl.B} H={inp.wl.H} dtype={inp.wl.dtype} splits={num_splits}", flush=True)
+    dev = to_device(inp)
+    cache = device_cache(inp, dev)
+    q_dtype = torch.float32 if inp.wl.dtype == "f32" else torch.bfloat16
+    step = DecodeStep(inp.wl.B, inp.wl.H, inp.wl.d_h, inp.wl.d_c, inp.wl.d_R, inp.wl.n_max, q_dtype, "cuda",
+                      num_splits=num_splits)
+    step(dev["q_C"], dev["q_R"], dev["W_UK"], dev["W_UV"], cache, dev["lens"])
+    torch.cuda.synchronize()
+    return {"q_abs": step.q_abs.float().cpu().numpy().astype(np.float64),
+            "o_lat": step.o_latent.cpu().numpy().astype(np.float64),
+            "lse": step.lse.cpu().numpy().astype(np.float64),
+            "o": step.out.cpu().numpy().astype(np.float64)}
+
+
+@pytest.mark.parametrize("name,splits", [("split", 0), ("split", 1), ("split", 37), ("h64", 0), ("h32", 5),
+                                         ("fp8", 0), ("paged", 9), ("f32-var", 0), ("packed", 4)])
+def test_step_with_fused_combine_uv(name, splits):
+    wl, lens = MINI[name]
+    inp = make_inputs(wl, lens=np.array(lens))
+    got = run_step(inp, num_splits=splits)
+    all_finite(got, inp)
+    compare(inp, got, oracle.decode(inp))
+
+
+def test_step_v3_b1_full():
+    inp = make_inputs(2)
+    got = run_step(inp)
+    all_finite(got, inp)
+    compare(inp, got, oracle.decode(inp))
