@@ -239,9 +239,9 @@ def main():
         c = copies[r % R]
         if name == "absorb":
             ops.mla_absorb_q(c["q_C"], c["W_UK"], out=step.q_abs, stream=stream)
-        elif name == "partial":
-            ops.mla_decode_partial(step.q_abs, c["q_R"], caches[r % R], c["lens"], wl.n_max, step.scale,
-                                   step.workspace, num_splits=args.num_splits, stream=stream)
+        elif name == "partial":   # as in the step: spare workgroups (small batch) warm W_UV
+            ops.mla_decode_partial_warm(step.q_abs, c["q_R"], caches[r % R], c["lens"], wl.n_max, step.scale,
+                                        step.workspace, c["W_UV"], num_splits=args.num_splits, stream=stream)
         elif name == "combine":
             ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent,
                                    step.lse, num_splits=args.num_splits, stream=stream)

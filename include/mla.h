@@ -182,6 +182,18 @@ int mla_decode_attn(const void* q_abs, const void* q_R, int q_dtype, const mla_c
 int mla_decode_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
                        const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
                        int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * mla_decode_partial_warm -- mla_decode_partial (same arguments, same result) that also pulls
+ * [warm, warm + warm_bytes) into the device's last-level cache: when the pass has fewer
+ * workgroups than the GPU has compute units (small batches), the spare workgroups read one word
+ * of every 128-byte line of that buffer and exit.  A decode step passes W_UV here so that the
+ * W_UV product after the combine reads it from the cache.  Nothing is written; results never
+ * depend on it.  warm: device pointer, 4-byte aligned (NULL with warm_bytes == 0 = no warm-up).
+ */
+int mla_decode_partial_warm(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                            const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                            int num_splits, void* workspace, size_t workspace_bytes, const void* warm,
+                            size_t warm_bytes, void* stream);
 int mla_decode_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
                        const void* workspace, size_t workspace_bytes, float* o_latent, float* lse, void* stream);
 

@@ -142,6 +142,19 @@ void k_partial_mfma(PartialArgs a) {
   __shared__ float alpha_s[2][NWAVE * 32];   // rescale factor of each head
   __shared__ __attribute__((aligned(16))) int flags_s[2][4];   // 1 if any of wave w's heads was rescaled
 
+  if ((int)blockIdx.x >= a.W) {
+    // one of the a.extra warm-up workgroups: read one word of every 128-byte line of its share of
+    // the warm-up buffer (the lines stay in the last-level cache for the next pass) and exit
+    const int64_t nlines = (a.warm_bytes + 127) / 128;
+    const int64_t per = (nlines + a.extra - 1) / a.extra;
+    const int64_t l0 = (int64_t)(blockIdx.x - a.W) * per, l1 = min(nlines, l0 + per);
+    const uint32_t* p = (const uint32_t*)a.warm;
+    const int64_t last_word = a.warm_bytes / 4 - 1;
+    uint32_t x = 0;
+    for (int64_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) x ^= p[min(l * 32, last_word)];
+    asm volatile("" : : "v"(x));   // consume the loads
+    return;
+  }
   build_tile_prefix(a.seq_lens, a.B, P, nullptr);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
@@ -653,7 +666,7 @@ void k_partial_mfma(PartialArgs a) {
 hipError_t launch_partial_mfma(const PartialArgs& a, bool fp8, bool paged, hipStream_t s) {
   const int nw = a.H / 32;
 #define MLA_LAUNCH(NW, F, PG)                                                              \
-  hipLaunchKernelGGL((k_partial_mfma<NW, F, PG>), dim3(a.W), dim3(NW * 64), 0, s, a); \
+  hipLaunchKernelGGL((k_partial_mfma<NW, F, PG>), dim3(a.W + a.extra), dim3(NW * 64), 0, s, a); \
   return hipGetLastError();
 #define MLA_BY_NW(F, PG)            \
   if (nw == 4) { MLA_LAUNCH(4, F, PG) } \

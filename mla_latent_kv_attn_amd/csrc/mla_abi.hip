@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mla_internal.h"
 
 namespace {
@@ -161,8 +163,16 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   pa->ws_acc = (float*)workspace;
   pa->ws_ml = (float*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
   pa->ws_prefix = (int*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H));
+  pa->warm = nullptr;
+  pa->warm_bytes = 0;
+  pa->extra = 0;
   return MLA_OK;
 }
+
+// MI355X compute units (one partial-pass workgroup fills one), and the most workgroups a partial
+// pass adds to warm a buffer (64 read a 16.8 MB weight well within a small-batch pass)
+constexpr int kCUs = 256;
+constexpr int kWarmWGs = 64;
 
 int launch_partial(const mla::PartialArgs& pa, bool generic, bool fp8, bool paged, hipStream_t s) {
   return hip_status(generic ? mla::launch_partial_f32(pa, s) : mla::launch_partial_mfma(pa, fp8, paged, s));
@@ -205,6 +215,26 @@ int mla_decode_partial(const void* q_abs, const void* q_R, int q_dtype, const ml
   int st = prepare_partial(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, num_splits,
                            workspace, workspace_bytes, &pa, &generic, &fp8, &paged);
   if (st != MLA_OK || B == 0) return st;
+  return launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
+}
+
+int mla_decode_partial_warm(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                            const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                            int num_splits, void* workspace, size_t workspace_bytes, const void* warm,
+                            size_t warm_bytes, void* stream) {
+  mla::PartialArgs pa;
+  bool generic = false, fp8 = false, paged = false;
+  int st = prepare_partial(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, num_splits,
+                           workspace, workspace_bytes, &pa, &generic, &fp8, &paged);
+  if (st != MLA_OK || B == 0) return st;
+  if (warm_bytes > 0 && !warm) return MLA_ERR_NULL;
+  if (warm_bytes > 0 && ((uintptr_t)warm & 3u) != 0) return MLA_ERR_UNSUPPORTED;
+  // up to kWarmWGs extra workgroups on otherwise idle CUs warm the buffer; the fp32 kernel has none
+  if (!generic && warm_bytes >= 4 && pa.W < kCUs) {
+    pa.warm = warm;
+    pa.warm_bytes = (int64_t)warm_bytes;
+    pa.extra = std::min(kWarmWGs, kCUs - pa.W);
+  }
   return launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
 }
 

@@ -37,6 +37,9 @@ struct PartialArgs {
   float* ws_acc;                // [slots, H, d_c]
   float* ws_ml;                 // [slots, H, 2]   (m in log2 units, l)
   int* ws_prefix;               // [B + 1] tile prefix sums (written by workgroup 0)
+  const void* warm;             // optional: buffer to pull into the cache with the spare workgroups
+  int64_t warm_bytes;
+  int extra;                    // workgroups launched beyond W (only used for the warm-up)
 };
 
 struct CombineArgs {

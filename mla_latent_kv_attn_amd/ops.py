@@ -168,6 +168,21 @@ def mla_decode_partial(q_abs, q_R, cache: Cache, seq_lens, max_len: int, scale: 
         _stream(stream, q_abs)))
 
 
+def mla_decode_partial_warm(q_abs, q_R, cache: Cache, seq_lens, max_len: int, scale: float, workspace, warm,
+                            num_splits: int = 0, stream=None) -> None:
+    """mla_decode_partial that also pulls the device tensor ``warm`` into the last-level cache with
+    its spare workgroups (see include/mla.h)."""
+    _dev(q_abs, q_R, seq_lens, workspace, warm)
+    B, H, d_c = q_abs.shape
+    d_R = q_R.shape[2]
+    if not warm.is_contiguous():
+        raise ValueError("warm must be contiguous")
+    check("mla_decode_partial_warm", _lib.lib().mla_decode_partial_warm(
+        q_abs.data_ptr(), q_R.data_ptr(), dtype_code(q_abs), ctypes.byref(cache.desc), seq_lens.data_ptr(),
+        int(max_len), B, H, d_c, d_R, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(),
+        warm.data_ptr(), warm.numel() * warm.element_size(), _stream(stream, q_abs)))
+
+
 def mla_decode_combine(seq_lens, max_len: int, B: int, H: int, d_c: int, workspace, o_latent, lse=None,
                        num_splits: int = 0, stream=None) -> None:
     """Combine pass of mla_decode_attn: workspace partials -> o_latent [B,H,d_c], lse [B,H]."""

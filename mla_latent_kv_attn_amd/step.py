@@ -1,5 +1,6 @@
 """One full absorbed decode step over preallocated buffers, all on one stream:
-mla_absorb_q -> mla_decode_partial -> mla_decode_combine_uv (the combine pass and mla_uv_out; one
+mla_absorb_q -> mla_decode_partial_warm (the partial pass; at small batch its spare workgroups pull
+W_UV into the last-level cache) -> mla_decode_combine_uv (the combine pass and mla_uv_out; one
 kernel at batch <= 4, two otherwise).  Buffers are allocated once (torch device memory) and
 reused, so a step is three or four kernel launches and nothing else."""
 from __future__ import annotations
@@ -26,8 +27,9 @@ class DecodeStep:
 
     def __call__(self, q_C, q_R, W_UK, W_UV, cache: "ops.Cache", seq_lens, stream=None):
         ops.mla_absorb_q(q_C, W_UK, out=self.q_abs, stream=stream)
-        ops.mla_decode_partial(self.q_abs, q_R, cache, seq_lens, self.max_len, self.scale, self.workspace,
-                               num_splits=self.num_splits, stream=stream)
+        # the partial pass warms W_UV into the cache with its spare workgroups (small batches)
+        ops.mla_decode_partial_warm(self.q_abs, q_R, cache, seq_lens, self.max_len, self.scale, self.workspace,
+                                    W_UV, num_splits=self.num_splits, stream=stream)
         ops.mla_decode_combine_uv(seq_lens, self.max_len, self.workspace, W_UV, self.o_latent, out=self.out,
                                   lse=self.lse, num_splits=self.num_splits, stream=stream)
         return self.out

@@ -154,3 +154,17 @@ def test_combine_uv_validation(lib):
     assert call(out=None) == L.MLA_ERR_NULL
     assert call(o_lat=FAKE + 4) == L.MLA_ERR_UNSUPPORTED
     assert call(B=0) == L.MLA_OK
+
+
+def test_partial_warm_validation(lib):
+    f = lib.mla_decode_partial_warm
+    d = _desc()
+    need = lib.mla_decode_workspace_bytes(1, 128, 512, 4096, 0)
+
+    def call(warm=FAKE, nbytes=1 << 20, ws=FAKE, B=1):
+        return f(FAKE, FAKE, L.MLA_BF16, ctypes.byref(d), FAKE, 4096, B, 128, 512, 64, 1 / math.sqrt(192), 0, ws, need,
+                 warm, nbytes, None)
+    assert call(ws=None) == L.MLA_ERR_WORKSPACE
+    assert call(warm=None) == L.MLA_ERR_NULL
+    assert call(warm=FAKE + 2) == L.MLA_ERR_UNSUPPORTED
+    assert call(B=0) == L.MLA_OK

@@ -303,3 +303,22 @@ def test_step_v3_b1_full():
     got = run_step(inp)
     all_finite(got, inp)
     compare(inp, got, oracle.decode(inp))
+
+
+@pytest.mark.parametrize("name", ["split", "fp8", "paged"])
+def test_partial_warm_changes_nothing(name):
+    """mla_decode_partial_warm (spare workgroups pull a buffer into the cache) leaves exactly the
+    workspace contents of mla_decode_partial."""
+    wl, lens = MINI[name]
+    inp = make_inputs(wl, lens=np.array(lens))
+    print(f"[gpu] partial warm {inp.wl.name}", flush=True)
+    dev = to_device(inp)
+    cache = device_cache(inp, dev)
+    q_abs = ops.mla_absorb_q(dev["q_C"], dev["W_UK"])
+    nbytes = ops.mla_decode_workspace_bytes(wl.B, wl.H, wl.d_c, wl.n_max, 5)
+    ws = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ops.mla_decode_partial(q_abs, dev["q_R"], cache, dev["lens"], wl.n_max, wl.scale, ws[0], num_splits=5)
+    ops.mla_decode_partial_warm(q_abs, dev["q_R"], cache, dev["lens"], wl.n_max, wl.scale, ws[1], dev["W_UV"],
+                                num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[0], ws[1])
