@@ -143,6 +143,7 @@ void k_partial_mfma(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) int flags_s[2][4];   // 1 if any of wave w's heads was rescaled
 
   if ((int)blockIdx.x >= a.W) {
+    if (blockIdx.y != 0) return;
     // one of the a.extra warm-up workgroups: read one word of every 128-byte line of its share of
     // the warm-up buffer (the lines stay in the last-level cache for the next pass) and exit
     const int64_t nlines = (a.warm_bytes + 127) / 128;
@@ -156,7 +157,7 @@ void k_partial_mfma(PartialArgs a) {
     return;
   }
   build_tile_prefix(a.seq_lens, a.B, P, nullptr);
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
   const int NT = P[a.B];
   const int Wp = min(a.W, NT);
@@ -285,7 +286,8 @@ void k_partial_mfma(PartialArgs a) {
   // ---------------------------------------------------------------- per-lane constants
   constexpr int CPW = 16 / NWAVE;           // 32-column blocks of the latent owned by each wave
   const int hf = lane >> 5;                 // lane half
-  const int h = wave * 32 + (lane & 31);    // this lane's head in the score phase
+  const int h0 = blockIdx.y * 32 * NWAVE;   // first head of this workgroup's head group
+  const int h = h0 + wave * 32 + (lane & 31);   // this lane's head in the score phase
   const int srow = pi_row(lane & 31);       // score-operand row (token within tile)
   const int G = lane >> 4;                  // 16-lane group
   // LDS read bases (bytes inside a stage); every k-step / column block adds an immediate offset
@@ -438,7 +440,7 @@ void k_partial_mfma(PartialArgs a) {
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless raised (m_run = -inf: 0)
     m_run = m_new;
     l_run *= alpha;
-    alpha_s[pb][h] = alpha;        // lanes l and l ^ 32 hold the same head and store the same value
+    alpha_s[pb][h - h0] = alpha;   // lanes l and l ^ 32 hold the same head and store the same value
     flags_s[pb][wave] = any;       // every lane stores the same value
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -645,7 +647,7 @@ void k_partial_mfma(PartialArgs a) {
       const int trow = ln >> 3, tchunk = ln & 7;
 #pragma unroll
       for (int hb = 0; hb < NWAVE; ++hb) {
-        float* dst = a.ws_acc + ((int64_t)(w + b) * H + hb * 32 + trow) * 512 + 32 * wave * CPW + 4 * tchunk;
+        float* dst = a.ws_acc + ((int64_t)(w + b) * H + h0 + hb * 32 + trow) * 512 + 32 * wave * CPW + 4 * tchunk;
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
           const f32x16& A = acc[hb * CPW + j];
@@ -658,15 +660,15 @@ void k_partial_mfma(PartialArgs a) {
             *(f32x4*)(dst + (8 * q) * 512 + 32 * j) = *(const f32x4*)(tb + (8 * q + trow) * 144 + 16 * tchunk);
         }
       }
-      if (ln < 32) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};
+      if (ln < 32) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + h0 + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};
     }
   }
 }
 
 hipError_t launch_partial_mfma(const PartialArgs& a, bool fp8, bool paged, hipStream_t s) {
-  const int nw = a.H / 32;
+  const int nw = a.H / 32 / a.hgroups;
 #define MLA_LAUNCH(NW, F, PG)                                                              \
-  hipLaunchKernelGGL((k_partial_mfma<NW, F, PG>), dim3(a.W + a.extra), dim3(NW * 64), 0, s, a); \
+  hipLaunchKernelGGL((k_partial_mfma<NW, F, PG>), dim3(a.W + a.extra, a.hgroups), dim3(NW * 64), 0, s, a); \
   return hipGetLastError();
 #define MLA_BY_NW(F, PG)            \
   if (nw == 4) { MLA_LAUNCH(4, F, PG) } \

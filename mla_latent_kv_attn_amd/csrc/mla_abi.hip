@@ -166,6 +166,10 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   pa->warm = nullptr;
   pa->warm_bytes = 0;
   pa->extra = 0;
+  // Few splits (small batches): split the heads of the MFMA pass into two groups of workgroups
+  // as well, so that each workgroup loads and stores half as much per tile (its fixed costs
+  // dominate there).  Two groups still fit on the chip for W <= 128.
+  pa->hgroups = (!*generic && H == 128 && W <= 128) ? 2 : 1;
   return MLA_OK;
 }
 
@@ -230,10 +234,10 @@ int mla_decode_partial_warm(const void* q_abs, const void* q_R, int q_dtype, con
   if (warm_bytes > 0 && !warm) return MLA_ERR_NULL;
   if (warm_bytes > 0 && ((uintptr_t)warm & 3u) != 0) return MLA_ERR_UNSUPPORTED;
   // up to kWarmWGs extra workgroups on otherwise idle CUs warm the buffer; the fp32 kernel has none
-  if (!generic && warm_bytes >= 4 && pa.W < kCUs) {
+  if (!generic && warm_bytes >= 4 && pa.W * pa.hgroups < kCUs) {
     pa.warm = warm;
     pa.warm_bytes = (int64_t)warm_bytes;
-    pa.extra = std::min(kWarmWGs, kCUs - pa.W);
+    pa.extra = std::min(kWarmWGs, kCUs - pa.W * pa.hgroups);
   }
   return launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
 }

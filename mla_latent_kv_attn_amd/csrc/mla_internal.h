@@ -40,6 +40,7 @@ struct PartialArgs {
   const void* warm;             // optional: buffer to pull into the cache with the spare workgroups
   int64_t warm_bytes;
   int extra;                    // workgroups launched beyond W (only used for the warm-up)
+  int hgroups;                  // MFMA pass: head groups (grid y); group g owns heads [g H/hgroups, ..)
 };
 
 struct CombineArgs {
