@@ -66,42 +66,47 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// absorb, small batch (B <= 4): a plain stream over W_UK (no reuse to exploit).  Grid (H, 4 column
-// quarters), 256 threads.  Thread t owns columns 8 (t % 16) .. +7 of its quarter and rows
-// t / 16 + 16 j (j = 0..7): eight 16-byte weight loads in flight per thread.  The 16 row groups
-// are summed through LDS.
+// absorb, small batch (B <= 4): a plain stream over W_UK (no reuse to exploit).  Grid (H, 8
+// column eighths), 256 threads.  Thread t owns columns 8 (t % 8) .. +7 of its eighth and rows
+// t / 8 + 32 j (j = 0..3): four 16-byte weight loads in flight per thread, issued first.  The
+// NB query rows of head h come through LDS; the 32 row groups are summed through LDS.
 // ---------------------------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(256) void k_absorb_gemv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
                                                      uint16_t* __restrict__ out, int B, int H) {
-  constexpr int kRed = 128 + 4;
-  __shared__ __attribute__((aligned(16))) float red[16 * NB * kRed];
-  const int h = blockIdx.x, quarter = blockIdx.y, tid = threadIdx.x;
-  const int cg = tid & 15, rg = tid >> 4;
-  const uint16_t* wp = w + ((int64_t)h * 128 + rg) * 512 + quarter * 128 + cg * 8;
-  u32x4 wv[8];
+  constexpr int kRed = 64 + 4;
+  __shared__ __attribute__((aligned(16))) float red[32 * NB * kRed];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[NB][128];
+  const int h = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid & 7, rg = tid >> 3;
+  const uint16_t* wp = w + ((int64_t)h * 128 + rg) * 512 + part * 64 + cg * 8;
+  u32x4 wv[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wv[j] = *(const u32x4*)(wp + (int64_t)j * 16 * 512);
-  float qv[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      qv[b][j] = b < B ? bf16_bits_to_f32(q[((int64_t)b * H + h) * 128 + rg + 16 * j]) : 0.f;
+  for (int j = 0; j < 4; ++j) wv[j] = *(const u32x4*)(wp + (int64_t)j * 32 * 512);
+  if (tid < 16 * NB) {
+    const int b = tid >> 4;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (b < B) v = *(const u32x4*)(q + ((int64_t)b * H + h) * 128 + 8 * (tid & 15));
+    *(u32x4*)&qs[b][8 * (tid & 15)] = v;
+  }
+  __syncthreads();
   float acc[NB][8];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 4; ++j) {
+    float qv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) qv[b] = bf16_bits_to_f32(qs[b][rg + 32 * j]);
 #pragma unroll
     for (int c2 = 0; c2 < 4; ++c2) {
       const float w0 = __uint_as_float(wv[j][c2] << 16), w1 = __uint_as_float(wv[j][c2] & 0xffff0000u);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        acc[b][2 * c2] = fmaf(qv[b][j], w0, acc[b][2 * c2]);
-        acc[b][2 * c2 + 1] = fmaf(qv[b][j], w1, acc[b][2 * c2 + 1]);
+        acc[b][2 * c2] = fmaf(qv[b], w0, acc[b][2 * c2]);
+        acc[b][2 * c2 + 1] = fmaf(qv[b], w1, acc[b][2 * c2 + 1]);
       }
     }
   }
@@ -112,19 +117,19 @@ __global__ __launch_bounds__(256) void k_absorb_gemv(const uint16_t* __restrict_
     *(float4*)(r + 4) = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
   }
   __syncthreads();
-  for (int o = tid; o < NB * 128; o += 256) {
-    const int b = o >> 7, col = o & 127;
+  for (int o = tid; o < NB * 64; o += 256) {
+    const int b = o >> 6, col = o & 63;
     if (b >= B) break;
     float v = 0.f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) v += red[(g * NB + b) * kRed + col];
-    out[((int64_t)b * H + h) * 512 + quarter * 128 + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+    for (int g = 0; g < 32; ++g) v += red[(g * NB + b) * kRed + col];
+    out[((int64_t)b * H + h) * 512 + part * 64 + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
   }
 }
 
 hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, int H, hipStream_t s) {
   if (B <= 4) {
-    const dim3 grid(H, 4);
+    const dim3 grid(H, 8);
     if (B == 1)
       hipLaunchKernelGGL(k_absorb_gemv<1>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
                          (uint16_t*)out, B, H);
