@@ -526,113 +526,6 @@ void k_partial_mfma(PartialArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
   };
-  // bf16 only: score(it) with the value MFMAs of tile it-1 (stage vst, probabilities vpb)
-  // interleaved, two after each score k-step pair for the first kVin pairs; the rest follow the
-  // score (with the softmax of tile it scheduled among them).  Value operands are loaded two pairs
-  // ahead.  The value MFMAs are numbered by step u = 0..15: group G = u / NWAVE is the latent
-  // column pair (ks, j0), hb = u % NWAVE the head block.  The caller has rescaled acc already.
-  auto score_value = [&](const uint8_t* st, TileSrc js, const uint8_t* vst, int vpb) __attribute__((always_inline)) -> f32x16 {
-    constexpr int kVin = 12;
-    constexpr int kAvBuf = NWAVE == 1 ? 3 : 2;
-    asm volatile("" : "+s"(js.lbase), "+s"(js.rbase), "+s"(js.sbase), "+s"(js.st), "+s"(js.last));
-    f32x16 S = {}, S2 = {};
-    auto lat_op = [&](int s) __attribute__((always_inline)) -> u32x4 { return *(const u32x4*)(st + sc_base + 32 * s); };
-    auto rope_op = [&](int q) __attribute__((always_inline)) -> u32x4 { return *(const u32x4*)(st + rope_base + 1024 * q); };
-    auto val_op = [&](int cb, int ks) __attribute__((always_inline)) -> u32x4 {
-      const uint8_t* p0 = vst + val_base + 16 * kLatStride * ks + 64 * cb;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLatStride));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      return u32x4{l2[0], l2[1], h2[0], h2[1]};
-    };
-    auto g_ks = [&](int G) __attribute__((always_inline)) { return G / (CPW / 2); };
-    auto g_j0 = [&](int G) __attribute__((always_inline)) { return 2 * (G % (CPW / 2)); };
-    auto val_pb = [&](int u) __attribute__((always_inline)) -> u32x4 {
-      return *(const u32x4*)(pbuf[vpb] + (u % NWAVE) * 32 * kPbStride + pb_base + 32 * g_ks(u / NWAVE));
-    };
-    u32x4 av0b[kAvBuf], av1b[kAvBuf], pbb[3];
-    // operands of the value steps that begin before pair 2
-#pragma unroll
-    for (int G = 0; G * NWAVE < 2 && G * NWAVE < kVin; ++G) {
-      av0b[G % kAvBuf] = val_op(wave * CPW + g_j0(G), g_ks(G));
-      av1b[G % kAvBuf] = val_op(wave * CPW + g_j0(G) + 1, g_ks(G));
-    }
-    pbb[0] = val_pb(0);
-    pbb[1] = val_pb(1);
-    constexpr int kPre = 2;   // the interleaved value MFMAs give the reads time
-    u32x4 pre[kPre];
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) pre[s] = lat_op(s);
-#pragma unroll
-    for (int s = 0; s < 32; s += 2) {
-      const int u = s / 2;
-      const u32x4 a0 = pre[s % kPre], a1 = pre[(s + 1) % kPre];
-      if (s + kPre < 32) {
-        pre[s % kPre] = lat_op(s + kPre);
-        pre[(s + 1) % kPre] = lat_op(s + kPre + 1);
-      }
-      if (u + 2 < kVin) {
-        const int un = u + 2;
-        if (un % NWAVE == 0) {
-          const int G = un / NWAVE;
-          av0b[G % kAvBuf] = val_op(wave * CPW + g_j0(G), g_ks(G));
-          av1b[G % kAvBuf] = val_op(wave * CPW + g_j0(G) + 1, g_ks(G));
-        }
-        pbb[un % 3] = val_pb(un);
-      }
-      asm volatile("" ::: "memory");
-      const u32x4 q0 = qf[s < QREG ? s : 0], q1 = qf[s + 1 < QREG ? s + 1 : 0];   // (bf16: QREG = 32)
-      if (s == 0) {
-        mfma_v_first(S, a0, q0);
-        mfma_v_first(S2, a1, q1);
-      } else {
-        mfma_v(S, a0, q0);
-        mfma_v(S2, a1, q1);
-      }
-      if (u < kVin) {
-        const int G = u / NWAVE, hb = u % NWAVE, j0 = g_j0(G);
-        acc[hb * CPW + j0] = mfma32x32x16(av0b[G % kAvBuf], pbb[u % 3], acc[hb * CPW + j0]);
-        acc[hb * CPW + j0 + 1] = mfma32x32x16(av1b[G % kAvBuf], pbb[u % 3], acc[hb * CPW + j0 + 1]);
-      }
-      {
-        const int k0 = u * LPT / 16, k1 = (u + 1) * LPT / 16;   // constants after unrolling
-        if (k0 < k1) {
-          uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
-          asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
-#pragma unroll
-          for (int k = k0; k < k1; ++k) job(js, k, vx0, vx1, vf0, vf1);
-        }
-      }
-    }
-    {
-      const uint8_t* qrow = qrs + wave * 4096 + qr_base;
-      const u32x4 b0 = *(const u32x4*)(qrow);
-      const u32x4 b1 = *(const u32x4*)(qrow + 1024);
-      const u32x4 b2 = *(const u32x4*)(qrow + 2048);
-      const u32x4 b3 = *(const u32x4*)(qrow + 3072);
-      const u32x4 r0 = rope_op(0), r1 = rope_op(1), r2 = rope_op(2), r3 = rope_op(3);
-      mfma_v(S, r0, b0);
-      mfma_v(S2, r1, b1);
-      mfma_v(S, r2, b2);
-      mfma_v(S2, r3, b3);
-    }
-    // remaining value steps
-#pragma unroll
-    for (int u = kVin; u < 16; ++u) {
-      const int G = u / NWAVE, hb = u % NWAVE, j0 = g_j0(G);
-      const u32x4 x0 = val_op(wave * CPW + j0, g_ks(G)), x1 = val_op(wave * CPW + j0 + 1, g_ks(G));
-      const u32x4 pv = val_pb(u);
-      acc[hb * CPW + j0] = mfma32x32x16(x0, pv, acc[hb * CPW + j0]);
-      acc[hb * CPW + j0 + 1] = mfma32x32x16(x1, pv, acc[hb * CPW + j0 + 1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
-    asm volatile("s_nop 15" : "+v"(S), "+v"(S2));   // wait states before VALU reads of S, S2
-#pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] += S2[i];
-    return S;
-  };
-
 
   // ---------------------------------------------------------------- pipeline
   // Tile it: wait for its loads, barrier (publishes the tile, the probabilities of tile it-1 and
@@ -715,18 +608,10 @@ void k_partial_mfma(PartialArgs a) {
       advance(nn);
       nsrc = locate(nn);
       const int nvalid = min(kTile, len_b - (tok_base + it * kTile));
-      if constexpr (!FP8 && NWAVE >= 2) {
-        rescale_with(fl, (it - 1) & 1);
-        const f32x16 S = score_value(stage(it), cur, stage(it - 1), (it - 1) & 1);
-        softmax(S, nvalid, stage(it), it & 1);
-      } else {
-        // fp8 (wider operands) and the single-wave variant (no registers to spare): score, then
-        // value
-        const f32x16 S = score(stage(it), std::integral_constant<bool, !FP8>{}, cur);
-        if constexpr (!FP8) rescale_with(fl, (it - 1) & 1);
-        value(stage(it - 1), (it - 1) & 1);
-        softmax(S, nvalid, stage(it), it & 1);
-      }
+      const f32x16 S = score(stage(it), std::integral_constant<bool, !FP8>{}, cur);
+      if constexpr (!FP8) rescale_with(fl, (it - 1) & 1);
+      value(stage(it - 1), (it - 1) & 1);
+      softmax(S, nvalid, stage(it), it & 1);
     }
     // the workgroup's last tile, if it is in this segment (nothing left to load)
     if (it < it_end) {
