@@ -34,9 +34,10 @@ hipError_t launch_absorb_f32(const float* q, const float* w, float* out, int B, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Partial pass, fp32 cache, any d_c <= 1024 and d_R <= 256.  Workgroup w walks the segments of its
-// tile range; for each head it runs an online softmax over 32-token tiles and writes the partial
-// (m, l, acc) into slot w + b.  Scores are kept in log2 units (s * scale * log2 e).
+// Partial pass, fp32 cache, any d_c <= 1024 and d_R <= 256.  Grid (W, H): workgroup (w, h) walks
+// the segments of tile range w for head h, running an online softmax over 32-token tiles (8
+// threads per token for the score, one column per thread for the weighted sum), and writes the
+// partial (m, l, acc) into slot w + b.  Scores are kept in log2 units (s * scale * log2 e).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ const float* row_f32(const float* base, int64_t sb, int64_t st, const int32_t* bt,
                                                 int page_size, int max_pages, int b, int tok) {
@@ -53,15 +54,16 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
   __shared__ float qs[1024 + 256];
   __shared__ float ss[kTile];
   build_tile_prefix(a.seq_lens, a.B, P, L);
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
   const int NT = P[a.B];
   const int Wp = min(a.W, NT);
-  const int w = blockIdx.x;
+  const int w = blockIdx.x, h = blockIdx.y;
   if (w >= Wp) return;
   const int t_begin = (int)((int64_t)w * NT / Wp);
   const int t_end = (int)((int64_t)(w + 1) * NT / Wp);
   const int tid = threadIdx.x;
+  const int tj = tid >> 3, tr = tid & 7;   // score phase: token tj of the tile, lane tr of its 8
   const int d_c = a.d_c, d_R = a.d_R, H = a.H;
   const float* qa = (const float*)a.q_abs;
   const float* qr = (const float*)a.q_R;
@@ -75,61 +77,63 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
     const int tok_lo = (t - P[b]) * kTile;
     const int tok_hi = min(L[b], (seg_end - P[b]) * kTile);
     const int slot = w + b;
-    for (int h = 0; h < H; ++h) {
+    __syncthreads();
+    for (int k = tid; k < d_c; k += blockDim.x) qs[k] = qa[((int64_t)b * H + h) * d_c + k];
+    for (int k = tid; k < d_R; k += blockDim.x) qs[d_c + k] = qr[((int64_t)b * H + h) * d_R + k];
+    __syncthreads();
+    float m = -INFINITY, l = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = tok_lo; t0 < tok_hi; t0 += kTile) {
+      const int n = min(kTile, tok_hi - t0);
+      // score of token tj: 8 lanes split the dot product, then a 3-step exchange
+      float sc = 0.f;
+      if (tj < n) {
+        const float* cr = row_f32(lat, a.lat_sb, a.lat_st, a.block_table, a.page_size, a.max_pages, b, t0 + tj);
+        const float* rr = row_f32(rope, a.rope_sb, a.rope_st, a.block_table, a.page_size, a.max_pages, b, t0 + tj);
+        for (int k = tr; k < d_c; k += 8) sc = fmaf(qs[k], cr[k], sc);
+        for (int k = tr; k < d_R; k += 8) sc = fmaf(qs[d_c + k], rr[k], sc);
+      }
+      sc += __shfl_xor(sc, 1, 64);
+      sc += __shfl_xor(sc, 2, 64);
+      sc += __shfl_xor(sc, 4, 64);
+      if (tj < n && tr == 0) ss[tj] = sc * a.sl2;
       __syncthreads();
-      for (int k = tid; k < d_c; k += blockDim.x) qs[k] = qa[((int64_t)b * H + h) * d_c + k];
-      for (int k = tid; k < d_R; k += blockDim.x) qs[d_c + k] = qr[((int64_t)b * H + h) * d_R + k];
+      float mx = -INFINITY;
+      for (int j = 0; j < n; ++j) mx = fmaxf(mx, ss[j]);
+      const float m_new = fmaxf(m, mx);
+      const float alpha = exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      for (int j = 0; j < n; ++j) {
+        const float p = exp2f(ss[j] - m_new);
+        l += p;
+        const float* cr = row_f32(lat, a.lat_sb, a.lat_st, a.block_table, a.page_size, a.max_pages, b, t0 + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = tid + i * 256;
+          if (k < d_c) acc[i] = fmaf(p, cr[k], acc[i]);
+        }
+      }
+      m = m_new;
       __syncthreads();
-      float m = -INFINITY, l = 0.f;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int t0 = tok_lo; t0 < tok_hi; t0 += kTile) {
-        const int n = min(kTile, tok_hi - t0);
-        if (tid < n) {
-          const float* cr = row_f32(lat, a.lat_sb, a.lat_st, a.block_table, a.page_size, a.max_pages, b, t0 + tid);
-          const float* rr = row_f32(rope, a.rope_sb, a.rope_st, a.block_table, a.page_size, a.max_pages, b, t0 + tid);
-          float s = 0.f;
-          for (int k = 0; k < d_c; ++k) s = fmaf(qs[k], cr[k], s);
-          for (int k = 0; k < d_R; ++k) s = fmaf(qs[d_c + k], rr[k], s);
-          ss[tid] = s * a.sl2;
-        }
-        __syncthreads();
-        float mx = -INFINITY;
-        for (int j = 0; j < n; ++j) mx = fmaxf(mx, ss[j]);
-        const float m_new = fmaxf(m, mx);
-        const float alpha = exp2f(m - m_new);
-        l *= alpha;
+    }
+    const int64_t o = ((int64_t)slot * H + h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-        for (int j = 0; j < n; ++j) {
-          const float p = exp2f(ss[j] - m_new);
-          l += p;
-          const float* cr = row_f32(lat, a.lat_sb, a.lat_st, a.block_table, a.page_size, a.max_pages, b, t0 + j);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int k = tid + i * 256;
-            if (k < d_c) acc[i] = fmaf(p, cr[k], acc[i]);
-          }
-        }
-        m = m_new;
-        __syncthreads();
-      }
-      const int64_t o = ((int64_t)slot * H + h);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = tid + i * 256;
-        if (k < d_c) a.ws_acc[o * d_c + k] = acc[i];
-      }
-      if (tid == 0) {
-        a.ws_ml[o * 2 + 0] = m;
-        a.ws_ml[o * 2 + 1] = l;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int k = tid + i * 256;
+      if (k < d_c) a.ws_acc[o * d_c + k] = acc[i];
+    }
+    if (tid == 0) {
+      a.ws_ml[o * 2 + 0] = m;
+      a.ws_ml[o * 2 + 1] = l;
     }
     t = seg_end;
   }
 }
 
 hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_partial_f32, dim3(a.W), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_partial_f32, dim3(a.W, a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -120,7 +120,7 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
 
   if (q_dtype == MLA_F32 && cache->latent_dtype == MLA_F32 && cache->rope_dtype == MLA_F32) {
-    if (d_c > 1024 || d_R > 256) return MLA_ERR_UNSUPPORTED;
+    if (d_c > 1024 || d_R > 256 || H > 65535) return MLA_ERR_UNSUPPORTED;
     *generic = true;
     *fp8 = false;
   } else if (q_dtype == MLA_BF16 && (cache->latent_dtype == MLA_BF16 || cache->latent_dtype == MLA_FP8_E4M3) &&
