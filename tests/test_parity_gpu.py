@@ -322,3 +322,42 @@ def test_partial_warm_changes_nothing(name):
                                 num_splits=5)
     torch.cuda.synchronize()
     assert torch.equal(ws[0], ws[1])
+
+
+@pytest.mark.parametrize("page", [32, 128, 256])
+def test_page_sizes(page):
+    """Paged caches with pages of 32, 128 and 256 tokens (a tile never straddles a page)."""
+    wl = WORKLOADS[4].with_(name=f"paged-p{page}", B=3, n_max=512, len_lo=1, len_hi=512, page_size=page)
+    inp = make_inputs(wl, lens=np.array([512, 100, 33]))
+    got = run_gpu(inp, num_splits=7)
+    all_finite(got, inp)
+    compare(inp, got, oracle.decode(inp))
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_padded_row_strides(cfg):
+    """Split caches whose rows and sequences are padded in memory (token stride 512 + 64 latent
+    elements, rope rows of 72, scales with a padded sequence stride): the strides come from the
+    cache descriptor, not from the widths."""
+    wl = WORKLOADS[cfg].with_(name=f"padded-{cfg}", B=3, n_max=160, len_lo=1, len_hi=160)
+    inp = make_inputs(wl, lens=np.array([160, 45, 0]))
+    print(f"[gpu] padded strides {wl.name}", flush=True)
+    dev = to_device(inp)
+    B, N = wl.B, wl.n_max
+    lat = torch.zeros((B, N + 3, wl.d_c + 64), dtype=dev["latent"].dtype, device="cuda")
+    lat[:, :N, :wl.d_c] = dev["latent"]
+    rope = torch.zeros((B, N + 5, wl.d_R + 8), dtype=dev["rope"].dtype, device="cuda")
+    rope[:, :N, :wl.d_R] = dev["rope"]
+    scale = None
+    if dev["scale"] is not None:
+        scale = torch.ones((B, N + 16), dtype=torch.float32, device="cuda")
+        scale[:, :N] = dev["scale"]
+        scale = scale[:, :N]
+    cache = ops.Cache.split(lat[:, :N, :wl.d_c], rope[:, :N, :wl.d_R], scale)
+    q_abs = ops.mla_absorb_q(dev["q_C"], dev["W_UK"])
+    o_lat, lse = ops.mla_decode_attn(q_abs, dev["q_R"], cache, dev["lens"], N, d_h=wl.d_h, num_splits=5)
+    o = ops.mla_uv_out(o_lat, dev["W_UV"])
+    torch.cuda.synchronize()
+    got = {"q_abs": q_abs.float().cpu().numpy().astype(np.float64), "o_lat": o_lat.cpu().numpy().astype(np.float64),
+           "lse": lse.cpu().numpy().astype(np.float64), "o": o.cpu().numpy().astype(np.float64)}
+    compare(inp, got, oracle.decode(inp))
