@@ -123,14 +123,16 @@ int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, i
  * is the number of partial-pass workgroups over the whole batch (0 = the
  * library's choice for (B, H, max_len), the same choice mla_decode_attn makes).
  * With W workgroups the workspace holds (W + B - 1) partial slots of H x d_c
- * float sums and H (max, sum) pairs, then B + 1 int32 tile prefix sums; each of
- * the three regions is rounded up to a multiple of 256 bytes.
- * Returns 0 for invalid sizes.
+ * float sums and H (max, sum) pairs, then B + 1 int32 tile prefix sums, then H
+ * int32 counters and min(B, 4) x H x 4 x 128 floats used by the one-kernel form
+ * of mla_decode_combine_uv; each of the five regions is rounded up to a multiple
+ * of 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits);
 
-/* The number of partial-pass workgroups mla_decode_attn uses when num_splits == 0: about one per
- * two 32-token tiles of the batch, ceil(B * ceil(max_len / 32) / 2), clamped to [1, 256]. */
+/* The number of partial-pass splits mla_decode_attn uses when num_splits == 0, from the tile
+ * count bound T = B * ceil(max_len / 32): for T <= 1024, about four tiles per split,
+ * min(ceil(T / 4), 64); otherwise about two, min(ceil(T / 2), 256); at least 1. */
 int mla_decode_auto_splits(int B, int H, int max_len);
 
 /*
@@ -201,10 +203,13 @@ int mla_decode_combine(const int32_t* seq_lens, int max_len, int B, int H, int d
  * mla_decode_combine_uv -- the combine pass followed by mla_uv_out, as one call: the same
  * arguments as mla_decode_combine (o_latent and lse are written exactly as there) plus W_UV
  * [H, d_h, d_c] in w_dtype and out [B, H, d_h] float32 (written), with the semantics of
- * mla_uv_out.  For a bf16 W_UV with d_h == 128, d_c == 512 and B <= 4 it is one kernel that
- * starts streaming W_UV while it merges the partials (at small batch both passes are
- * latency-bound); otherwise it launches the two passes.  Errors as for mla_decode_combine and
- * mla_uv_out; nothing is launched when validation fails.
+ * mla_uv_out.  For a bf16 W_UV with d_h == 128, d_c == 512 and B <= 4 it is one kernel: four
+ * workgroups per head each merge a quarter of the latent columns and multiply it with the
+ * matching quarter of W_UV, and the last of the four to finish adds the four products in a
+ * fixed order (a device-scope counter in the workspace, which the partial pass zeroes, so this
+ * form must follow a partial pass on the same workspace); otherwise it launches the two passes.
+ * Results are the same whichever workgroup finishes last.  Errors as for mla_decode_combine
+ * and mla_uv_out; nothing is launched when validation fails.
  */
 int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
                           const void* workspace, size_t workspace_bytes, const void* W_UV, int w_dtype, int d_h,

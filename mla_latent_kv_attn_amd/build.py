@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_amd.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_abi.hip", "decode_generic.hip", "absorb_uv_mfma.hip", "decode_partial_mfma.hip"]
+SOURCES = ["mla_abi.hip", "decode_generic.hip", "absorb_uv_mfma.hip", "decode_partial_mfma.hip",
+           "decode_partial_small.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -32,6 +33,12 @@ CFLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-lambda-capture",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+# Per-source extra flags.  The small-batch partial kernel keeps its output accumulator in VGPRs
+# (it needs about 220 registers in all): with AGPR accumulators the compiler copies the whole
+# accumulator between register classes on every tile around the conditional rescale.
+EXTRA_FLAGS = {"decode_partial_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -44,7 +51,7 @@ def hipcc() -> str:
 # Kernels whose DMA pipeline counts outstanding vector-memory operations (s_waitcnt vmcnt): a
 # spill to scratch memory inside them would add scratch loads/stores to that count, so they must
 # use no scratch (SGPR spills into VGPR lanes are fine).
-NO_SCRATCH_KERNELS = ("k_partial_mfma",)
+NO_SCRATCH_KERNELS = ("k_partial_mfma", "k_partial_small")
 
 
 def _check_spills(src: str, remarks: str) -> None:
@@ -63,7 +70,8 @@ def _check_spills(src: str, remarks: str) -> None:
 
 def _compile(src: str, save_temps: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)

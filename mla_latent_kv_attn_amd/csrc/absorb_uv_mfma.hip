@@ -274,96 +274,94 @@ __global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat
 }
 
 // ---------------------------------------------------------------------------------------------
-// Combine + uv in one pass, small batch (B <= 4, d_h = 128, d_c = 512, row-major workspace).
-// Grid (H), 1024 threads (16 waves); the workgroup owns head h:
-//   1. wave w starts the loads of W_UV[h] rows 8w .. 8w+7 (lane l: columns 8l .. 8l+7) right
-//      after those of the first sequence's partials, so the weight stream overlaps step 2;
-//   2. per sequence b: the log-sum-exp merge of the segments' (m, l) and partial rows of head h
-//      into o_lat[b,h]: eight groups of 128 threads (one float4 column each) take every eighth
-//      segment, their first eight loads issued before the (m, l) reduction, and are summed
-//      through LDS; o_lat is kept in LDS and also written to o_latent (and lse);
-//   3. out[b,h,i] = W_UV[h][i] . o_lat[b,h] with the halving exchange of k_uv_gemv.
+// Combine + uv, small batch (B <= 4, d_h = 128, d_c = 512, row-major workspace).
+// Grid (H, 4), 256 threads.  Workgroup (h, q) owns latent columns 128q .. 128q+127 of head h, so
+// each one reads a quarter of the head's partial rows and of W_UV[h] (the per-CU load rate, not
+// HBM, bounds this pass at small batch, so the work is spread over four times as many CUs):
+//   1. per sequence b: the log-sum-exp merge of the segments' (m, l) and of the quarter's partial
+//      columns into o_lat[b,h, quarter]: eight groups of 32 threads (one float4 column each) take
+//      every eighth segment and are summed through LDS in group order; written to o_latent
+//      (lse by the q = 0 workgroup);
+//   2. y_q[b,i] = sum over the quarter's columns c of W_UV[h][i][c] o_lat[b,h,c], i = 0..127
+//      (thread pair 2i, 2i+1 takes 64 columns each), stored to the workspace;
+//   3. the last of the four workgroups of head h to finish adds the four quarters in the order
+//      q = 0..3 and writes out[b,h,:].  The quarters are exchanged with device-coherent stores and
+//      loads (agent-scope atomic accesses: they reach the coherence point without the whole-cache
+//      write-back and invalidate of a device-scope fence), and the stores have completed
+//      (s_waitcnt) before a device-scope counter is raised; the partial pass zeroes the counter
+//      and the last workgroup resets it.  The summation order is fixed, so the result does not
+//      depend on which workgroup finishes last.
 // ---------------------------------------------------------------------------------------------
 template <int NB>
-__global__ __launch_bounds__(1024) void k_combine_uv(CombineArgs a, const uint16_t* __restrict__ w,
-                                                     float* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_t* __restrict__ w,
+                                                    float* __restrict__ out) {
   constexpr int kW = 1024;   // segment weights kept in LDS
-  __shared__ __attribute__((aligned(16))) float ol[NB][512];
-  __shared__ float4 part[7][128];
+  __shared__ __attribute__((aligned(16))) float olq[NB][128];
+  __shared__ float4 part[7][32];
   __shared__ float wts[kW];
-  __shared__ float rr[16];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float rr[4];
+  __shared__ int last_s;
+  const int h = blockIdx.x, q = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H;
-  // weight rows of this wave (8 rows x 16 B per lane), loaded after the first sequence's partials:
-  // loads complete in issue order, and the partials are needed first
-  u32x4 wv[8];
   const int NT = a.ws_prefix[a.B];
-  const int c4 = tid & 127, sg = tid >> 7;
+  const int c4 = tid & 31, sg = tid >> 5;
+  const int64_t sstride = (int64_t)H * 512;
+  u32x4 wv[8];   // W_UV[h][tid >> 1][128q + 64 (tid & 1) .. +63], loaded after the first partial rows
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     if (b >= a.B) break;
     const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1];
-    float* orow = a.o_latent + ((int64_t)b * H + h) * 512;
+    float* orow = a.o_latent + ((int64_t)b * H + h) * 512 + 128 * q;
     const bool empty = Pb1 == Pb;
     const int Wp = max(1, min(a.W, NT));
     const int w0 = empty ? 0 : (int)(((int64_t)(Pb + 1) * Wp + NT - 1) / NT) - 1;   // owner of tile t: ceil((t+1)Wp/NT)-1
     const int w1 = empty ? -1 : (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
     const int nseg = w1 - w0 + 1;
     const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml[s H]
-    const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 4 * c4;   // + s H 512
-    const int64_t sstride = (int64_t)H * 512;
-    // the partial rows of the first 64 segments do not depend on the weights: start their loads
-    // before the (m, l) reduction, so that both round trips overlap
+    const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 128 * q + 4 * c4;   // + s H 512
     const float2 q0 = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
-    float4 x[8];
+    float4 x[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int su = sg + 8 * u;
       x[u] = su < nseg ? *(const float4*)(src + su * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (b == 0) {
-      const uint16_t* wp = w + ((int64_t)h * 128 + wave * 8) * 512 + 8 * lane;
+      const uint16_t* wp = w + ((int64_t)h * 128 + (tid >> 1)) * 512 + 128 * q + 64 * (tid & 1);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) wv[r] = *(const u32x4*)(wp + r * 512);
+      for (int k = 0; k < 8; ++k) wv[k] = *(const u32x4*)(wp + 8 * k);
     }
     if (empty) {
       if (sg == 0) {
-        *(float4*)&ol[b][4 * c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4*)&olq[b][4 * c4] = make_float4(0.f, 0.f, 0.f, 0.f);
         *(float4*)(orow + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
+      if (a.lse && q == 0 && tid == 0) a.lse[(int64_t)b * H + h] = -INFINITY;
       continue;
     }
     float mloc = q0.x;
-    for (int s = tid + 1024; s < nseg; s += 1024) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
+    for (int s = tid + 256; s < nseg; s += 256) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, d, 64));
     if (lane == 0) rr[wave] = mloc;
     __syncthreads();
-    float M = rr[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) M = fmaxf(M, rr[i]);
+    const float M = fmaxf(fmaxf(rr[0], rr[1]), fmaxf(rr[2], rr[3]));
     __syncthreads();
     float lloc = 0.f;
-    if (tid < nseg) {
-      const float f = exp2f(q0.x - M);
-      wts[tid] = f;
-      lloc = f * q0.y;
-    }
-    for (int s = tid + 1024; s < nseg; s += 1024) {
-      const float2 q = ml[(int64_t)s * H];
-      lloc += exp2f(q.x - M) * q.y;
+    for (int s = tid; s < nseg; s += 256) {
+      const float2 mls = s == tid ? q0 : ml[(int64_t)s * H];
+      const float f = exp2f(mls.x - M);
+      if (s < kW) wts[s] = f;
+      lloc += f * mls.y;
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) lloc += __shfl_xor(lloc, d, 64);
     if (lane == 0) rr[wave] = lloc;
     __syncthreads();
-    float Ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Ls += rr[i];
+    const float Ls = (rr[0] + rr[1]) + (rr[2] + rr[3]);
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int su = sg + 8 * u;
       const float f = su < nseg ? wts[su] : 0.f;
       o.x = fmaf(f, x[u].x, o.x);
@@ -371,7 +369,7 @@ __global__ __launch_bounds__(1024) void k_combine_uv(CombineArgs a, const uint16
       o.z = fmaf(f, x[u].z, o.z);
       o.w = fmaf(f, x[u].w, o.w);
     }
-    for (int s = sg + 64; s < nseg; s += 8) {
+    for (int s = sg + 32; s < nseg; s += 8) {
       const float4 xs = *(const float4*)(src + s * sstride);
       const float f = s < kW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M);
       o.x = fmaf(f, xs.x, o.x);
@@ -392,63 +390,69 @@ __global__ __launch_bounds__(1024) void k_combine_uv(CombineArgs a, const uint16
       }
       const float inv = 1.f / Ls;
       const float4 r = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-      *(float4*)&ol[b][4 * c4] = r;
+      *(float4*)&olq[b][4 * c4] = r;
       *(float4*)(orow + 4 * c4) = r;
     }
-    if (a.lse && tid == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
+    if (a.lse && q == 0 && tid == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
     __syncthreads();   // part / rr / wts are reused by the next sequence
   }
   __syncthreads();
-  // 3. out[b, h, 8 wave + r] for r in 0..7
-  float x[NB][8];
+  // 2. this quarter's share of out[b, h, i], i = tid >> 1: 64 columns per thread, pair sum
+  float* yq = a.ws_uv + (int64_t)h * 4 * 128;   // [b][h][q][i]
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const float4 x0 = *(const float4*)&ol[b][8 * lane], x1 = *(const float4*)&ol[b][8 * lane + 4];
-    x[b][0] = x0.x; x[b][1] = x0.y; x[b][2] = x0.z; x[b][3] = x0.w;
-    x[b][4] = x1.x; x[b][5] = x1.y; x[b][6] = x1.z; x[b][7] = x1.w;
-  }
-  constexpr int K = NB * 8;
-  constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : 5;
-  float v[K];
+    if (b >= a.B) break;
+    const float* xo = &olq[b][64 * (tid & 1)];
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) {
-        acc = fmaf(x[b][2 * c2], __uint_as_float(wv[r][c2] << 16), acc);
-        acc = fmaf(x[b][2 * c2 + 1], __uint_as_float(wv[r][c2] & 0xffff0000u), acc);
-      }
-      v[b * 8 + r] = acc;
+    for (int k = 0; k < 8; ++k) {
+      const float4 xa = *(const float4*)(xo + 8 * k), xb = *(const float4*)(xo + 8 * k + 4);
+      acc0 = fmaf(xa.x, __uint_as_float(wv[k][0] << 16), acc0);
+      acc1 = fmaf(xa.y, __uint_as_float(wv[k][0] & 0xffff0000u), acc1);
+      acc0 = fmaf(xa.z, __uint_as_float(wv[k][1] << 16), acc0);
+      acc1 = fmaf(xa.w, __uint_as_float(wv[k][1] & 0xffff0000u), acc1);
+      acc0 = fmaf(xb.x, __uint_as_float(wv[k][2] << 16), acc0);
+      acc1 = fmaf(xb.y, __uint_as_float(wv[k][2] & 0xffff0000u), acc1);
+      acc0 = fmaf(xb.z, __uint_as_float(wv[k][3] << 16), acc0);
+      acc1 = fmaf(xb.w, __uint_as_float(wv[k][3] & 0xffff0000u), acc1);
     }
+    float t = acc0 + acc1;
+    t += __shfl_xor(t, 1, 64);
+    // device-coherent store (agent-scope atomic store: written through to the coherence point,
+    // so no cache write-back is needed before the counter below is raised)
+    if ((tid & 1) == 0)
+      __hip_atomic_store(yq + (int64_t)b * H * 512 + q * 128 + (tid >> 1), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // 3. publish: every store of this workgroup has completed before the counter is raised; the
+  // last workgroup of head h reads the four quarters with device-coherent loads and adds them in
+  // order q = 0..3
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) last_s = __hip_atomic_fetch_add(a.ws_cnt + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 3;
+  __syncthreads();
+  if (!last_s) return;
+  if (tid < 128) {
 #pragma unroll
-  for (int step = 0; step < LK; ++step) {
-    const int d = 32 >> step;
-    const int half = K >> (step + 1);
-    const bool upper = (lane & d) != 0;
+    for (int b = 0; b < NB; ++b) {
+      if (b >= a.B) break;
+      float* y = yq + (int64_t)b * H * 512 + tid;
+      float yv[4];
 #pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, d, 64);
+      for (int k = 0; k < 4; ++k) yv[k] = __hip_atomic_load(y + 128 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      out[((int64_t)b * H + h) * 128 + tid] = ((yv[0] + yv[1]) + yv[2]) + yv[3];
     }
   }
-  float t = v[0];
-#pragma unroll
-  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
-  const int idx = (lane >> (6 - LK)) & (K - 1);
-  const int b = idx >> 3, r = idx & 7;
-  if ((lane & ((64 >> LK) - 1)) == 0 && b < a.B) out[((int64_t)b * H + h) * 128 + wave * 8 + r] = t;
+  if (tid == 0) __hip_atomic_store(a.ws_cnt + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s) {
+  const dim3 grid(a.H, 4);
   if (a.B == 1)
-    hipLaunchKernelGGL(k_combine_uv<1>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+    hipLaunchKernelGGL(k_combine_uv<1>, grid, dim3(256), 0, s, a, (const uint16_t*)w, out);
   else if (a.B == 2)
-    hipLaunchKernelGGL(k_combine_uv<2>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+    hipLaunchKernelGGL(k_combine_uv<2>, grid, dim3(256), 0, s, a, (const uint16_t*)w, out);
   else
-    hipLaunchKernelGGL(k_combine_uv<4>, dim3(a.H), dim3(1024), 0, s, a, (const uint16_t*)w, out);
+    hipLaunchKernelGGL(k_combine_uv<4>, grid, dim3(256), 0, s, a, (const uint16_t*)w, out);
   return hipGetLastError();
 }
 

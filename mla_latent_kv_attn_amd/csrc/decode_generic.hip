@@ -54,8 +54,10 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
   __shared__ float qs[1024 + 256];
   __shared__ float ss[kTile];
   build_tile_prefix(a.seq_lens, a.B, P, L);
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];  // for the combine pass
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];
+    for (int i = threadIdx.x; i < a.H; i += blockDim.x) a.ws_cnt[i] = 0;
+  }
   const int NT = P[a.B];
   const int Wp = min(a.W, NT);
   const int w = blockIdx.x, h = blockIdx.y;

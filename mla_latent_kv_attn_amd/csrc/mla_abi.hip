@@ -20,17 +20,21 @@ int hip_status(hipError_t e) {
 bool known_dtype(int d) { return d == MLA_F32 || d == MLA_BF16 || d == MLA_FP8_E4M3; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Partial-pass workgroups when the caller passes 0: one workgroup per CU for large batches
-// (the kernel runs one workgroup per CU), fewer for short single-sequence work so that each
-// workgroup owns at least four 32-token tiles.
-// About two 32-token tiles per workgroup, at most one workgroup per CU (256).  At small batch
-// the partial pass is latency-bound and more splits shorten it, until the combine pass's reads
-// of the (W + B - 1) x H x d_c partials outweigh the gain (measured at B = 1, N = 4096: 64 splits).
+// Batches of at most kSmallTiles 32-token tiles in total (bf16) take the small-batch partial
+// kernel: one 32-head block per workgroup, so H/32 workgroups share each split.
+constexpr int64_t kSmallTiles = 1024;
+
+int64_t total_tiles_bound(int B, int max_len) { return (int64_t)B * ((max_len + mla::kTile - 1) / mla::kTile); }
+
+// Partial-pass splits when the caller passes 0.
+//  * small batches: about four tiles per split, at most 64 splits (with the V3 head count the
+//    four head blocks of 64 splits fill the 256 CUs); fewer splits also mean fewer partials for
+//    the combine pass to read;
+//  * otherwise about two tiles per split, at most one workgroup per CU (256).
 int auto_splits(int B, int H, int max_len) {
   (void)H;
-  const int64_t nt = (int64_t)B * ((max_len + mla::kTile - 1) / mla::kTile);
-  int64_t w = (nt + 1) / 2;
-  if (w > 256) w = 256;
+  const int64_t nt = total_tiles_bound(B, max_len);
+  int64_t w = nt <= kSmallTiles ? std::min<int64_t>((nt + 3) / 4, 64) : std::min<int64_t>((nt + 1) / 2, 256);
   if (w < 1) w = 1;
   return (int)w;
 }
@@ -161,15 +165,18 @@ int prepare_partial(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   pa->W = W;
   pa->sl2 = scale * 1.4426950408889634f;
   pa->ws_acc = (float*)workspace;
-  pa->ws_ml = (float*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
-  pa->ws_prefix = (int*)((char*)workspace + mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H));
+  pa->ws_ml = (float*)((char*)workspace + mla::ws_ml_off(W, B, H, d_c));
+  pa->ws_prefix = (int*)((char*)workspace + mla::ws_prefix_off(W, B, H, d_c));
+  pa->ws_cnt = (int*)((char*)workspace + mla::ws_cnt_off(W, B, H, d_c));
   pa->warm = nullptr;
   pa->warm_bytes = 0;
   pa->extra = 0;
-  // Few splits (small batches): split the heads of the MFMA pass into two groups of workgroups
-  // as well, so that each workgroup loads and stores half as much per tile (its fixed costs
-  // dominate there).  Two groups still fit on the chip for W <= 128.
-  pa->hgroups = (!*generic && H == 128 && W <= 128) ? 2 : 1;
+  // Small bf16 batches: the small-batch kernel, one workgroup per (split, 32-head block).
+  // Otherwise, with few splits, the heads of the large-batch kernel are split into two groups of
+  // workgroups, so that each workgroup loads and stores half as much per tile (its fixed costs
+  // dominate there); two groups still fit on the chip for W <= 128.
+  pa->small = (!*generic && !*fp8 && B <= mla::kSmallMaxB && total_tiles_bound(B, max_len) <= kSmallTiles) ? 1 : 0;
+  pa->hgroups = pa->small ? H / 32 : (!*generic && H == 128 && W <= 128) ? 2 : 1;
   return MLA_OK;
 }
 
@@ -179,7 +186,9 @@ constexpr int kCUs = 256;
 constexpr int kWarmWGs = 64;
 
 int launch_partial(const mla::PartialArgs& pa, bool generic, bool fp8, bool paged, hipStream_t s) {
-  return hip_status(generic ? mla::launch_partial_f32(pa, s) : mla::launch_partial_mfma(pa, fp8, paged, s));
+  if (generic) return hip_status(mla::launch_partial_f32(pa, s));
+  if (pa.small) return hip_status(mla::launch_partial_small(pa, paged, s));
+  return hip_status(mla::launch_partial_mfma(pa, fp8, paged, s));
 }
 
 int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c, int num_splits,
@@ -200,8 +209,10 @@ int prepare_combine(const int32_t* seq_lens, int max_len, int B, int H, int d_c,
   ca->d_c = d_c;
   ca->W = W;
   ca->ws_acc = (const float*)workspace;
-  ca->ws_ml = (const float*)((const char*)workspace + mla::ws_acc_bytes(W, B, H, d_c));
-  ca->ws_prefix = (const int*)((const char*)workspace + mla::ws_acc_bytes(W, B, H, d_c) + mla::ws_ml_bytes(W, B, H));
+  ca->ws_ml = (const float*)((const char*)workspace + mla::ws_ml_off(W, B, H, d_c));
+  ca->ws_prefix = (const int*)((const char*)workspace + mla::ws_prefix_off(W, B, H, d_c));
+  ca->ws_cnt = (int*)((char*)workspace + mla::ws_cnt_off(W, B, H, d_c));
+  ca->ws_uv = (float*)((char*)workspace + mla::ws_uv_off(W, B, H, d_c));
   ca->o_latent = o_latent;
   ca->lse = lse;
   return MLA_OK;
@@ -238,6 +249,10 @@ int mla_decode_partial_warm(const void* q_abs, const void* q_R, int q_dtype, con
     pa.warm = warm;
     pa.warm_bytes = (int64_t)warm_bytes;
     pa.extra = std::min(kWarmWGs, kCUs - pa.W * pa.hgroups);
+    // keep the block-index stride W + extra a multiple of 8 (one XCD per split in the
+    // small-batch kernel) when that leaves a warm-up workgroup
+    const int r = (pa.W + pa.extra) % 8;
+    if (r != 0 && pa.extra > r) pa.extra -= r;
   }
   return launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
 }

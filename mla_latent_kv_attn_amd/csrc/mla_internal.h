@@ -20,6 +20,7 @@ namespace mla {
 // ----------------------------------------------------------------------------------------------
 constexpr int kTile = 32;
 constexpr int kMaxB = 2048;
+constexpr int kSmallMaxB = 256;   // batch limit of the small-batch partial kernel (tile prefix in LDS)
 
 struct PartialArgs {
   const void* q_abs;            // [B, H, d_c]
@@ -37,10 +38,12 @@ struct PartialArgs {
   float* ws_acc;                // [slots, H, d_c]
   float* ws_ml;                 // [slots, H, 2]   (m in log2 units, l)
   int* ws_prefix;               // [B + 1] tile prefix sums (written by workgroup 0)
+  int* ws_cnt;                  // [H] counters of the fused combine + uv pass, zeroed by workgroup 0
   const void* warm;             // optional: buffer to pull into the cache with the spare workgroups
   int64_t warm_bytes;
   int extra;                    // workgroups launched beyond W (only used for the warm-up)
   int hgroups;                  // MFMA pass: head groups (grid y); group g owns heads [g H/hgroups, ..)
+  int small;                    // bf16: the small-batch kernel (one 32-head block per workgroup)
 };
 
 struct CombineArgs {
@@ -50,14 +53,16 @@ struct CombineArgs {
   const float* ws_acc;
   const float* ws_ml;
   const int* ws_prefix;         // [B + 1] tile prefix sums from the partial pass
+  int* ws_cnt;                  // [H] fused combine + uv: finished quarters per head (0 on entry)
+  float* ws_uv;                 // [min(B, 4), H, 4, 128] fused combine + uv: per-quarter outputs
   float* o_latent;              // [B, H, d_c]
   float* lse;                   // [B, H] or nullptr
 };
 
-// workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, each
-// 256-byte aligned.  A slot of the acc block holds H x d_c floats, row-major [slot][H][d_c]: the
-// partial pass writes whole 128-byte lines of a head's row, and a head's partial is contiguous
-// for the combine.
+// workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, then the
+// counters and per-quarter outputs of the fused combine + uv pass, each 256-byte aligned.  A slot
+// of the acc block holds H x d_c floats, row-major [slot][H][d_c]: the partial pass writes whole
+// 128-byte lines of a head's row, and a head's partial is contiguous for the combine.
 inline size_t ws_slots(int W, int B) { return (size_t)W + (size_t)B - 1; }
 inline size_t ws_acc_bytes(int W, int B, int H, int d_c) {
   size_t b = ws_slots(W, B) * (size_t)H * (size_t)d_c * sizeof(float);
@@ -68,9 +73,19 @@ inline size_t ws_ml_bytes(int W, int B, int H) {
   return (b + 255) & ~(size_t)255;
 }
 inline size_t ws_prefix_bytes(int B) { return (((size_t)B + 1) * sizeof(int) + 255) & ~(size_t)255; }
-inline size_t ws_total_bytes(int W, int B, int H, int d_c) {
-  return ws_acc_bytes(W, B, H, d_c) + ws_ml_bytes(W, B, H) + ws_prefix_bytes(B);
+inline size_t ws_cnt_bytes(int H) { return ((size_t)H * sizeof(int) + 255) & ~(size_t)255; }
+inline size_t ws_uv_bytes(int B, int H) {
+  const size_t nb = B < 4 ? (size_t)B : 4;
+  return (nb * (size_t)H * 4 * 128 * sizeof(float) + 255) & ~(size_t)255;
 }
+inline size_t ws_total_bytes(int W, int B, int H, int d_c) {
+  return ws_acc_bytes(W, B, H, d_c) + ws_ml_bytes(W, B, H) + ws_prefix_bytes(B) + ws_cnt_bytes(H) + ws_uv_bytes(B, H);
+}
+// byte offsets of the regions after the acc block
+inline size_t ws_ml_off(int W, int B, int H, int d_c) { return ws_acc_bytes(W, B, H, d_c); }
+inline size_t ws_prefix_off(int W, int B, int H, int d_c) { return ws_ml_off(W, B, H, d_c) + ws_ml_bytes(W, B, H); }
+inline size_t ws_cnt_off(int W, int B, int H, int d_c) { return ws_prefix_off(W, B, H, d_c) + ws_prefix_bytes(B); }
+inline size_t ws_uv_off(int W, int B, int H, int d_c) { return ws_cnt_off(W, B, H, d_c) + ws_cnt_bytes(H); }
 
 // launchers (return the launch error; host-side validation happens in mla_abi.cpp)
 hipError_t launch_absorb_f32(const float* q, const float* w, float* out, int B, int H, int d_h, int d_c,
@@ -78,6 +93,7 @@ hipError_t launch_absorb_f32(const float* q, const float* w, float* out, int B, 
 hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, int H, hipStream_t s);
 hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s);
 hipError_t launch_partial_mfma(const PartialArgs& a, bool fp8, bool paged, hipStream_t s);
+hipError_t launch_partial_small(const PartialArgs& a, bool paged, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_uv_f32w(const float* o_lat, const float* w, float* out, int B, int H, int d_h, int d_c,
                           hipStream_t s);

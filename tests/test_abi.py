@@ -59,11 +59,17 @@ def test_workspace_size_formula(lib):
         acc = (slots * H * d_c * 4 + 255) // 256 * 256
         ml = (slots * H * 2 * 4 + 255) // 256 * 256
         prefix = ((B + 1) * 4 + 255) // 256 * 256
-        assert ws(B, H, d_c, N, S) == acc + ml + prefix
-    # the auto choice: about two 32-token tiles per workgroup, at most 256 workgroups
-    assert lib.mla_decode_auto_splits(1, 128, 4096) == 64
-    assert lib.mla_decode_auto_splits(1, 128, 4095) == 64
+        cnt = (H * 4 + 255) // 256 * 256
+        uv = (min(B, 4) * H * 4 * 128 * 4 + 255) // 256 * 256
+        assert ws(B, H, d_c, N, S) == acc + ml + prefix + cnt + uv
+    # the auto choice: up to 1024 tiles of 32 tokens in total, about four tiles per split and at
+    # most 64 splits; beyond that about two tiles per split, at most 256
+    assert lib.mla_decode_auto_splits(1, 128, 4096) == 32
+    assert lib.mla_decode_auto_splits(1, 128, 4095) == 32
     assert lib.mla_decode_auto_splits(1, 128, 64) == 1
+    assert lib.mla_decode_auto_splits(32, 128, 1024) == 64
+    assert lib.mla_decode_auto_splits(33, 128, 1024) == 256
+    assert lib.mla_decode_auto_splits(8, 128, 1024) == 64
     assert lib.mla_decode_auto_splits(64, 128, 8192) == 256
     assert lib.mla_decode_auto_splits(1, 128, 1) == 1
 

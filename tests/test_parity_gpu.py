@@ -361,3 +361,21 @@ def test_padded_row_strides(cfg):
     got = {"q_abs": q_abs.float().cpu().numpy().astype(np.float64), "o_lat": o_lat.cpu().numpy().astype(np.float64),
            "lse": lse.cpu().numpy().astype(np.float64), "o": o.cpu().numpy().astype(np.float64)}
     compare(inp, got, oracle.decode(inp))
+
+
+@pytest.mark.parametrize("H,splits", [(128, 100), (128, 0), (64, 0), (32, 0)])
+def test_large_batch_kernel_variants(H, splits):
+    """Batches past the small-batch switch (more than 1024 tiles of 32 tokens) take the
+    large-batch kernel: 128 heads in one workgroup (4 waves), in two head groups when there are
+    at most 128 splits, and the 64- and 32-head variants.  Sampled comparison."""
+    B, n_max = 40, 1100
+    wl = WORKLOADS[3].with_(name=f"large-h{H}-s{splits}", B=B, H=H, n_max=n_max, len_lo=1, len_hi=n_max)
+    rng = np.random.default_rng(11)
+    lens = rng.integers(1, n_max + 1, size=B)
+    lens[:4] = [n_max, 0, 1, 33]
+    inp = make_inputs(wl, lens=lens)
+    got = run_gpu(inp, num_splits=splits)
+    all_finite(got, inp)
+    pairs = _sample_pairs(inp)
+    ref = oracle.decode(inp, pairs=pairs)
+    compare(inp, got, ref, pairs=pairs)
