@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "k_uv_bf16": "absorb_uv_mfma.hip",
     "k_uv_gemv": "absorb_uv_mfma.hip",
     "k_partial_mfma": "decode_partial_mfma.hip",
+    "k_partial_small": "decode_partial_small.hip",
     "k_combine_rows": "decode_generic.hip",
     "k_combine_heads": "decode_generic.hip",
     "k_combine_uv": "absorb_uv_mfma.hip",
@@ -51,7 +52,10 @@ def fused_combine_uv(wl):
 def kernel_names(wl):
     """Kernel that each pass launches for this workload (the library's own dispatch rules)."""
     small = wl.B <= 4
-    return {"absorb": "k_absorb_gemv" if small else "k_absorb_bf16", "partial": "k_partial_mfma",
+    tiles = wl.B * ((wl.n_max + 31) // 32)
+    small_partial = wl.dtype == "bf16" and wl.B <= 256 and tiles <= 1024
+    return {"absorb": "k_absorb_gemv" if small else "k_absorb_bf16",
+            "partial": "k_partial_small" if small_partial else "k_partial_mfma",
             "combine": "k_combine_heads" if (wl.H // 32) * wl.B >= 256 else "k_combine_rows",
             "uv": "k_uv_gemv" if small else "k_uv_bf16", "combine_uv": "k_combine_uv"}
 
@@ -76,8 +80,9 @@ def source_hash(fname: str) -> str:
     p = os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", fname)
     with open(p, "rb") as f:
         h = hashlib.sha256(f.read())
-    with open(os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", "mla_internal.h"), "rb") as f:
-        h.update(f.read())
+    for hdr in ("mla_internal.h", "partial_common.h"):
+        with open(os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", hdr), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

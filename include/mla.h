@@ -131,8 +131,8 @@ int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, i
 size_t mla_decode_workspace_bytes(int B, int H, int d_c, int max_len, int num_splits);
 
 /* The number of partial-pass splits mla_decode_attn uses when num_splits == 0, from the tile
- * count bound T = B * ceil(max_len / 32): for T <= 1024, about four tiles per split,
- * min(ceil(T / 4), 64); otherwise about two, min(ceil(T / 2), 256); at least 1. */
+ * count bound T = B * ceil(max_len / 32): for T <= 1024, min(ceil(3 T / 8), 64); otherwise
+ * about two tiles per split, min(ceil(T / 2), 256); at least 1. */
 int mla_decode_auto_splits(int B, int H, int max_len);
 
 /*

@@ -20,8 +20,9 @@
 //    rescale factors and a flag to LDS;
 //  * value: wave w multiplies its columns by the probabilities of all 32 heads (8 MFMA per tile
 //    into 64 accumulator registers; transposing LDS reads give the latent operand).
-// Software pipeline, one barrier per tile: iteration i runs value(i-1), softmax(i), score(i+1);
-// the barrier publishes the score partials of tile i and the probabilities of tile i-1.  The
+// Software pipeline, one barrier per tile: iteration i runs score(i+1), value(i-1), softmax(i),
+// with the MFMAs of the first two issued before the VALU work of the softmax; the barrier
+// publishes the score partials of tile i and the probabilities of tile i-1.  The
 // four head-block workgroups of a split sit on one XCD (block index stride a multiple of 8), so
 // a tile comes from HBM once and from that XCD's L2 for the other three.
 #include "partial_common.h"
@@ -186,13 +187,14 @@ void k_partial_small(PartialArgs a) {
 
   // score partial of this wave for the tile in stage st -> sbuf[par] (head-major rows of 128 B,
   // 16-byte chunk c of head n at position c ^ ((n >> 1) & 7))
-  auto score_part = [&](int stg, int par) __attribute__((always_inline)) {
+  // (score_mfma issues the MFMAs; score_store, later, writes the result: the MFMAs run while the
+  // wave does other work)
+  auto score_mfma = [&](int stg, f32x16& S0, f32x16& S1) __attribute__((always_inline)) {
     const uint8_t* st = my_ring + stg * NWAVE * kSlice;
     u32x4 av[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) av[j] = *(const u32x4*)(st + sc_row + 16 * ((2 * j + hf) ^ sc_x));
     const u32x4 rv = *(const u32x4*)(st + rope_rd);
-    f32x16 S0, S1;
     mfma_v_first(S0, av[0], qf[0]);
     mfma_v_first(S1, av[1], qf[1]);
 #pragma unroll
@@ -201,6 +203,8 @@ void k_partial_small(PartialArgs a) {
       mfma_v(S1, av[j + 1], qf[j + 1]);
     }
     mfma_v(S0, rv, qf[8]);
+  };
+  auto score_store = [&](f32x16& S0, f32x16& S1, int par) __attribute__((always_inline)) {
     asm volatile("s_nop 15" : "+v"(S0), "+v"(S1));
     const f32x16 S = S0 + S1;
     uint8_t* sb = sbuf[par] + wave * 4096 + hl * 128;
@@ -273,16 +277,19 @@ void k_partial_small(PartialArgs a) {
     }
   };
 
-  // partial of the segment of sequence b (accumulator, m, l) -> workspace slot w + b.  The
-  // accumulator blocks are transposed through LDS: the last segment uses this wave's ring slices
-  // (no tile is in flight any more; all four blocks at once), an earlier one this wave's part of
-  // sbuf[par] (free at this point; one block at a time).
-  auto flush = [&](int b, int par, bool final_seg) __attribute__((always_inline)) {
+  // partial of the segment of sequence b -> workspace slot w + b: flush_ml writes the (m, l) pairs
+  // of this wave's softmax heads, flush the accumulator.  The accumulator blocks are transposed
+  // through LDS: the last segment uses this wave's ring slices (no tile is in flight any more; all
+  // four blocks at once), an earlier one this wave's part of sbuf[par] (free at this point; one
+  // block at a time).
+  auto flush_ml = [&](int b) __attribute__((always_inline)) {
     float l_tot = l_part;
     l_tot += __shfl_xor(l_tot, 1, 64);
     l_tot += __shfl_xor(l_tot, 2, 64);
     l_tot += __shfl_xor(l_tot, 4, 64);
     if (sc == 0) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + h0 + sn) * 2) = f32x2{m_run, l_tot};
+  };
+  auto flush = [&](int b, int par, bool final_seg) __attribute__((always_inline)) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int trow = ln >> 3, tch = ln & 7;
@@ -328,7 +335,12 @@ void k_partial_small(PartialArgs a) {
   // compiler, which does not see the tile loads, adds its own wait for the query loads here)
   if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  score_part(0, 0);
+  {
+    f32x16 S0, S1;
+    score_mfma(0, S0, S1);
+    if (ntiles > 2) issue(2);   // after the query wait the compiler put before the MFMAs
+    score_store(S0, S1, 0);
+  }
   // Segment bookkeeping (uniform, in registers): the sequence of the tile whose value step comes
   // next and the first tile of the sequence after it; the same for the softmax step, with the
   // token index of that tile and the sequence length.  LDS lookups happen only at segment ends.
@@ -337,46 +349,57 @@ void k_partial_small(PartialArgs a) {
   int b_sm = b_val, sm_next = val_next;
   int sm_tok = __builtin_amdgcn_readfirstlane((t_begin - P[b_sm]) * kTile);
   int sm_len = __builtin_amdgcn_readfirstlane(Ls[b_sm]);
+  // Iteration it: the score MFMAs of tile it + 1 and the value MFMAs of tile it - 1 are issued
+  // first, then the loads of tile it + 2 (into the stage tile it - 1 just left); the softmax of
+  // tile it (VALU and LDS work) runs while the MFMAs execute; then the end of a segment is written
+  // out and the score partial of tile it + 1 is stored.
   for (int it = 0; it <= ntiles; ++it) {
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
     lds_barrier();
-    if (it >= 1) {
-      // value(it - 1); at the end of its sequence's segment, write the partial and reset
-      value((it - 1) % kNst, (it - 1) & 1);
-      if (it == ntiles || t_begin + it >= val_next) {
-        flush(b_val, (it - 1) & 1, it == ntiles);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-        m_run = -INFINITY;
-        l_part = 0.f;
-        if (it < ntiles) {
-          while (t_begin + it >= val_next) val_next = __builtin_amdgcn_readfirstlane(P[++b_val + 1]);
-        }
-      }
+    if (it < ntiles && t_begin + it >= sm_next) {   // the softmax enters a new sequence
+      while (t_begin + it >= sm_next) sm_next = __builtin_amdgcn_readfirstlane(P[++b_sm + 1]);
+      sm_tok = 0;
+      sm_len = __builtin_amdgcn_readfirstlane(Ls[b_sm]);
     }
-    if (it + 2 < ntiles) issue(it + 2);   // into the stage tile it - 1 just left (stage 2 at it = 0)
-    if (it < ntiles) {
-      if (t_begin + it >= sm_next) {   // softmax enters a new sequence
-        while (t_begin + it >= sm_next) sm_next = __builtin_amdgcn_readfirstlane(P[++b_sm + 1]);
-        sm_tok = 0;
-        sm_len = __builtin_amdgcn_readfirstlane(Ls[b_sm]);
-      }
-      softmax(it & 1, min(kTile, sm_len - sm_tok));
-      sm_tok += kTile;
-    }
-    if (it + 1 < ntiles) {
-      // score(it + 1); a new sequence first loads its folded query
-      const bool new_seq = t_begin + it + 1 >= sm_next;
-      if (new_seq) {
+    const bool do_score = it + 1 < ntiles;
+    f32x16 S0, S1;
+    if (do_score) {
+      // tile it + 1 has landed once only tile 2's loads may be outstanding (issued before the
+      // loop); a new sequence first loads its folded query
+      if (t_begin + it + 1 >= sm_next) {
         load_q(seq_of(it + 1));
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      } else if (it + 2 < ntiles) {
+      } else if (it == 0 && ntiles > 2) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
-      score_part((it + 1) % kNst, (it + 1) & 1);
+      score_mfma((it + 1) % kNst, S0, S1);
     }
+    bool seg_end = false;
+    if (it >= 1) {
+      value((it - 1) % kNst, (it - 1) & 1);
+      if (it + 2 < ntiles) issue(it + 2);
+      seg_end = it == ntiles || t_begin + it >= val_next;
+      if (seg_end) {
+        flush_ml(b_val);
+        m_run = -INFINITY;
+        l_part = 0.f;
+      }
+    }
+    if (it < ntiles) {
+      softmax(it & 1, min(kTile, sm_len - sm_tok));
+      sm_tok += kTile;
+    }
+    if (seg_end) {
+      flush(b_val, (it - 1) & 1, it == ntiles);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+      if (it < ntiles) {
+        while (t_begin + it >= val_next) val_next = __builtin_amdgcn_readfirstlane(P[++b_val + 1]);
+      }
+    }
+    if (do_score) score_store(S0, S1, (it + 1) & 1);
   }
 }
 

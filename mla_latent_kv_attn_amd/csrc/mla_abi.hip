@@ -27,14 +27,15 @@ constexpr int64_t kSmallTiles = 1024;
 int64_t total_tiles_bound(int B, int max_len) { return (int64_t)B * ((max_len + mla::kTile - 1) / mla::kTile); }
 
 // Partial-pass splits when the caller passes 0.
-//  * small batches: about four tiles per split, at most 64 splits (with the V3 head count the
-//    four head blocks of 64 splits fill the 256 CUs); fewer splits also mean fewer partials for
-//    the combine pass to read;
+//  * small batches: about 8/3 tiles per split, ceil(3 T / 8), at most 64 splits (with the V3 head
+//    count the four head blocks of 64 splits fill the 256 CUs).  Fewer splits mean fewer partials
+//    for the combine pass to read and spare CUs for the weight warm-up; more splits shorten the
+//    partial pass (measured at B = 1, N = 4096: 48 splits);
 //  * otherwise about two tiles per split, at most one workgroup per CU (256).
 int auto_splits(int B, int H, int max_len) {
   (void)H;
   const int64_t nt = total_tiles_bound(B, max_len);
-  int64_t w = nt <= kSmallTiles ? std::min<int64_t>((nt + 3) / 4, 64) : std::min<int64_t>((nt + 1) / 2, 256);
+  int64_t w = nt <= kSmallTiles ? std::min<int64_t>((3 * nt + 7) / 8, 64) : std::min<int64_t>((nt + 1) / 2, 256);
   if (w < 1) w = 1;
   return (int)w;
 }

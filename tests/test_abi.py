@@ -62,11 +62,12 @@ def test_workspace_size_formula(lib):
         cnt = (H * 4 + 255) // 256 * 256
         uv = (min(B, 4) * H * 4 * 128 * 4 + 255) // 256 * 256
         assert ws(B, H, d_c, N, S) == acc + ml + prefix + cnt + uv
-    # the auto choice: up to 1024 tiles of 32 tokens in total, about four tiles per split and at
-    # most 64 splits; beyond that about two tiles per split, at most 256
-    assert lib.mla_decode_auto_splits(1, 128, 4096) == 32
-    assert lib.mla_decode_auto_splits(1, 128, 4095) == 32
+    # the auto choice: up to 1024 tiles of 32 tokens in total, ceil(3 T / 8) splits, at most 64;
+    # beyond that about two tiles per split, at most 256
+    assert lib.mla_decode_auto_splits(1, 128, 4096) == 48
+    assert lib.mla_decode_auto_splits(1, 128, 4095) == 48
     assert lib.mla_decode_auto_splits(1, 128, 64) == 1
+    assert lib.mla_decode_auto_splits(1, 128, 96) == 2
     assert lib.mla_decode_auto_splits(32, 128, 1024) == 64
     assert lib.mla_decode_auto_splits(33, 128, 1024) == 256
     assert lib.mla_decode_auto_splits(8, 128, 1024) == 64
