@@ -19,6 +19,9 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
                    absorption identities of "Grouped-query and latent attention".
   merge_partials   pinned: equals one-pass softmax for every split of the tokens.
   cache_size.*     pinned: every cache-size figure printed on the pages.
+  cache_write.*    pinned: closed forms and invariants of the cache write (the new
+                   token's latent W_DKV h and rotated rope key RoPE_pos(W_KR h), and
+                   their bf16 / E4M3 storage forms), tests/test_oracle_cache_write.py.
   decode_bf16 / decode_e4m3  pinned: OCP FP8 special values, bf16 bit patterns.
   The rotary pairing convention of the input generator is not fixed by the
   pages: parity unpinned for that convention (both sides consume the same
@@ -29,3 +32,4 @@ from .mla_decode import (  # noqa: F401
     merge_partials, relative_l2,
 )
 from . import cache_size  # noqa: F401
+from . import cache_write  # noqa: F401
