@@ -227,6 +227,41 @@ int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, in
 int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out, int B, int H, int d_h,
                int d_c, void* stream);
 
+/*
+ * Workspace (device bytes) mla_cache_append needs: (D / 512) x B x 576 float32 partial sums of
+ * the projection.  Returns 0 for unsupported sizes (B < 1, D not a positive multiple of 512).
+ */
+size_t mla_cache_append_workspace_bytes(int B, int D);
+
+/*
+ * mla_cache_append -- write each sequence's new token into its cache row, the step before the
+ * attention pass ("MLA storage: Representing KV with a small latent vector", sections "Forming
+ * head-specific K and V from a small vector" and "Storing a positional key separately";
+ * "Grouped-query and latent attention", section "Why a separate rotary key"):
+ *   latent   c_b   = W_DKV h_b
+ *   rope key k_R,b = RoPE_pos[b](W_KR h_b): pair (2i, 2i+1) turned by pos[b] * rope_base^(-2i/d_R)
+ * stored at row pos[b] of sequence b in the cache described by `cache` (the same descriptor the
+ * attention pass reads; its latent, rope and latent_scale buffers are WRITTEN, only at that row).
+ *   h        [B, D] bf16      hidden states of the new tokens
+ *   W_DKV    [d_c, D] bf16    (row i maps h to latent component i)
+ *   W_KR     [d_R, D] bf16
+ *   dtype    MLA_BF16 (the dtype of h and both weights)
+ *   pos      [B] int32 device: row index (0-based position) of each new token; must lie inside
+ *            the cache (contiguous: below its per-sequence capacity; paged: a valid block-table
+ *            entry).  Not validated (that would need a host sync).
+ *   workspace device buffer of at least mla_cache_append_workspace_bytes(B, D) bytes,
+ *            16-byte aligned, any contents; overwritten
+ * fp32 accumulation; rope angles in double precision.  Storage: MLA_BF16 latent and rope are
+ * rounded to nearest even; an MLA_FP8_E4M3 latent stores OCP E4M3 codes RNE(clamp(c/s, +-448))
+ * with the float32 scale s = amax/448 over the row (s = 1 when the row is zero) in latent_scale.
+ * Supported: d_c == 512, d_R == 64, D a multiple of 512, rope MLA_BF16, latent MLA_BF16 or
+ * MLA_FP8_E4M3, contiguous or paged, 16-byte aligned pointers and rows, B <= 65535.  B == 0 is a
+ * no-op.  Two kernel launches on `stream`; deterministic.
+ */
+int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dtype, const int32_t* pos,
+                     const mla_cache_desc* cache, int B, int D, int d_c, int d_R, float rope_base, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

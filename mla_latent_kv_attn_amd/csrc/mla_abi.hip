@@ -317,3 +317,58 @@ int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, in
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t mla_cache_append_workspace_bytes(int B, int D) {
+  if (B < 1 || D < 512 || (D % 512) != 0) return 0;
+  return mla::append_ws_bytes(B, D);
+}
+
+int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dtype, const int32_t* pos,
+                     const mla_cache_desc* cache, int B, int D, int d_c, int d_R, float rope_base, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (B < 0 || D < 1 || d_c < 1 || d_R < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!cache) return MLA_ERR_NULL;
+  if (!known_dtype(cache->latent_dtype) || !known_dtype(cache->rope_dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(rope_base) || !(rope_base > 0.f)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!h || !W_DKV || !W_KR || !pos || !cache->latent || !cache->rope) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || cache->rope_dtype != MLA_BF16 ||
+      !(cache->latent_dtype == MLA_BF16 || cache->latent_dtype == MLA_FP8_E4M3))
+    return MLA_ERR_UNSUPPORTED;
+  if (d_c != 512 || d_R != 64 || D < 512 || (D % 512) != 0 || B > 65535) return MLA_ERR_UNSUPPORTED;
+  const bool fp8 = cache->latent_dtype == MLA_FP8_E4M3;
+  const bool paged = cache->block_table != nullptr;
+  if (fp8 && !cache->latent_scale) return MLA_ERR_NULL;
+  if (cache->latent_stride_tok < 1 || cache->rope_stride_tok < 1 || cache->latent_stride_b < 0 ||
+      cache->rope_stride_b < 0 || (fp8 && cache->scale_stride_b < 0))
+    return MLA_ERR_SHAPE;
+  if (paged && (cache->page_size < 1 || cache->max_pages < 1)) return MLA_ERR_SHAPE;
+  const int les = fp8 ? 1 : 2;
+  if (!aligned16(h) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(cache->latent) ||
+      !aligned16(cache->rope) || ((cache->latent_stride_tok * les) % 16) != 0 ||
+      ((cache->latent_stride_b * les) % 16) != 0 || ((cache->rope_stride_tok * 2) % 16) != 0 ||
+      ((cache->rope_stride_b * 2) % 16) != 0 || (fp8 && ((uintptr_t)cache->latent_scale & 3u) != 0))
+    return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < mla::append_ws_bytes(B, D)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  mla::AppendArgs a;
+  a.latent = const_cast<void*>(cache->latent);
+  a.rope = const_cast<void*>(cache->rope);
+  a.latent_scale = const_cast<float*>(cache->latent_scale);
+  a.block_table = cache->block_table;
+  a.lat_sb = cache->latent_stride_b;
+  a.lat_st = cache->latent_stride_tok;
+  a.rope_sb = cache->rope_stride_b;
+  a.rope_st = cache->rope_stride_tok;
+  a.scale_sb = cache->scale_stride_b;
+  a.page_size = paged ? cache->page_size : 1;
+  a.max_pages = paged ? cache->max_pages : 0;
+  a.rope_base = rope_base;
+  return hip_status(mla::launch_append(h, W_DKV, W_KR, pos, B, D, a, fp8, paged, (float*)workspace,
+                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -59,6 +59,17 @@ struct CombineArgs {
   float* lse;                   // [B, H] or nullptr
 };
 
+// cache write: destination rows (element strides as in mla_cache_desc)
+struct AppendArgs {
+  void* latent;
+  void* rope;
+  float* latent_scale;
+  const int32_t* block_table;
+  int64_t lat_sb, lat_st, rope_sb, rope_st, scale_sb;
+  int page_size, max_pages;
+  float rope_base;
+};
+
 // workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, then the
 // counters and per-quarter outputs of the fused combine + uv pass, each 256-byte aligned.  A slot
 // of the acc block holds H x d_c floats, row-major [slot][H][d_c]: the partial pass writes whole
@@ -101,6 +112,9 @@ hipError_t launch_uv_bf16w_generic(const float* o_lat, const void* w, float* out
                                    int d_c, hipStream_t s);
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s);
 hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s);
+size_t append_ws_bytes(int B, int D);
+hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
+                         const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s);
 
 }  // namespace mla
 

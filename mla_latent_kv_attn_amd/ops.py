@@ -223,3 +223,24 @@ def mla_uv_out(o_latent: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.T
                                               out.data_ptr(), B, H, d_h, d_c, _stream(stream, o_latent)))
     return out
 
+
+def mla_cache_append_workspace_bytes(B: int, D: int) -> int:
+    return int(_lib.lib().mla_cache_append_workspace_bytes(B, D))
+
+
+def mla_cache_append(h: torch.Tensor, W_DKV: torch.Tensor, W_KR: torch.Tensor, pos: torch.Tensor, cache: Cache,
+                     rope_base: float = 10000.0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write each sequence's new token into cache row pos[b]: latent W_DKV h[b], rope key
+    RoPE_pos[b](W_KR h[b]).  h [B, D] bf16, W_DKV [d_c, D], W_KR [d_R, D] bf16, pos [B] int32."""
+    _dev(h, W_DKV, W_KR, pos, workspace)
+    B, D = h.shape
+    d_c, d_R = W_DKV.shape[0], W_KR.shape[0]
+    if not (h.is_contiguous() and W_DKV.is_contiguous() and W_KR.is_contiguous() and pos.is_contiguous()):
+        raise ValueError("h, W_DKV, W_KR and pos must be contiguous")
+    if pos.dtype != torch.int32:
+        raise TypeError("pos is int32")
+    if workspace is None:
+        workspace = torch.empty(max(mla_cache_append_workspace_bytes(B, D), 1), dtype=torch.uint8, device=h.device)
+    check("mla_cache_append", _lib.lib().mla_cache_append(
+        h.data_ptr(), W_DKV.data_ptr(), W_KR.data_ptr(), dtype_code(h), pos.data_ptr(), ctypes.byref(cache.desc), B,
+        D, d_c, d_R, float(rope_base), workspace.data_ptr(), workspace.numel(), _stream(stream, h)))

@@ -175,3 +175,36 @@ def test_partial_warm_validation(lib):
     assert call(warm=None) == L.MLA_ERR_NULL
     assert call(warm=FAKE + 2) == L.MLA_ERR_UNSUPPORTED
     assert call(B=0) == L.MLA_OK
+
+
+def test_cache_append_validation(lib):
+    f = lib.mla_cache_append
+    ws = lib.mla_cache_append_workspace_bytes
+    assert ws(1, 7168) == 14 * 1 * 576 * 4 and ws(128, 7168) == 14 * 128 * 576 * 4
+    assert ws(0, 7168) == 0 and ws(1, 7000) == 0 and ws(1, 0) == 0
+    good_ws = ws(4, 7168)
+
+    def call(desc, B=4, D=7168, d_c=512, d_R=64, base=10000.0, dtype=L.MLA_BF16, h=FAKE, wsp=FAKE, wsb=good_ws,
+             pos=FAKE):
+        return f(h, FAKE, FAKE, dtype, pos, ctypes.byref(desc), B, D, d_c, d_R, base, wsp, wsb, None)
+
+    d = _desc()
+    assert call(d, B=-1) == L.MLA_ERR_SHAPE
+    assert call(d, base=0.0) == L.MLA_ERR_SHAPE
+    assert call(d, base=math.inf) == L.MLA_ERR_SHAPE
+    assert call(d, dtype=7) == L.MLA_ERR_DTYPE
+    assert call(d, B=0, h=None, pos=None) == L.MLA_OK                   # no-op
+    assert call(d, pos=None) == L.MLA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, L.MLA_BF16, FAKE, None, 4, 7168, 512, 64, 1e4, FAKE, good_ws, None) == L.MLA_ERR_NULL
+    assert call(d, dtype=L.MLA_F32) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, d_c=256) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, d_R=32) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, D=7000) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, h=FAKE + 2) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, wsp=None) == L.MLA_ERR_WORKSPACE
+    assert call(d, wsb=good_ws - 1) == L.MLA_ERR_WORKSPACE
+    assert call(d, wsp=FAKE + 4) == L.MLA_ERR_UNSUPPORTED
+    assert call(_desc(latent_dtype=L.MLA_F32)) == L.MLA_ERR_UNSUPPORTED
+    assert call(_desc(latent_dtype=L.MLA_FP8_E4M3)) == L.MLA_ERR_NULL     # fp8 needs the scale
+    assert call(_desc(st_tok=577)) == L.MLA_ERR_UNSUPPORTED               # unaligned rows
+    assert call(_desc(bt=FAKE, page=0, max_pages=4)) == L.MLA_ERR_SHAPE   # paged without a page size
