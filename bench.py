@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--row", choices=["decode", "append"], default="decode",
+                    help="decode: the absorbed decode step (default); append: the cache write of one step")
+    ap.add_argument("--append-batch", type=int, default=1, help="--row append: new tokens (sequences) per call")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
     return ap.parse_args()
@@ -168,6 +171,10 @@ def main():
         ms = ca.elapsed_time(cb) / 4
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5, "copy_ms": round(ms, 4),
                           "read_plus_write_TBps": round(2 * n / (ms * 1e-3) / 1e12, 3)}), flush=True)
+        return
+
+    if args.row == "append":
+        main_append(args)
         return
 
     from mla_latent_kv_attn_amd import ops
@@ -306,6 +313,97 @@ def main():
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def main_append(args):
+    """The cache write of one decode step (mla_cache_append) at the V3 shape: B new tokens, hidden
+    size 7168, latent 512 and rope key 64 written as bf16 into a split cache.  Weights are rotated
+    over enough copies to miss the 256 MB Infinity Cache; one HIP graph holds one call per copy."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_attn_amd import ops
+    from workloads.append import make_append_inputs
+
+    B, D, N = args.append_batch, 7168, 64
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    inp = make_append_inputs(B, D)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = {"h": bf16(inp.h), "W_DKV": bf16(inp.W_DKV), "W_KR": bf16(inp.W_KR)}
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(1, min(128, math.ceil(args.rotate_mb * 1e6 / per_copy)))
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    pos = torch.from_numpy((np.arange(B) * 7 + 3).astype(np.int32) % N).to(dev)
+    lat = torch.zeros((B, N, 512), dtype=torch.bfloat16, device=dev)
+    rope = torch.zeros((B, N, 64), dtype=torch.bfloat16, device=dev)
+    cache = ops.Cache.split(lat, rope)
+    ws = torch.empty(ops.mla_cache_append_workspace_bytes(B, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def one(i):
+        c = copies[i % R]
+        ops.mla_cache_append(c["h"], c["W_DKV"], c["W_KR"], pos, cache, workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, R)):
+            one(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(R):
+            one(i)
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / R))
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    calls = reps * R
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    alg = 576 * D * 2 + B * D * 2 + B * 4 + B * (512 + 64) * 2     # weights, h, positions, the new rows
+    achieved = alg / (us * 1e-6) / 1e9
+    out = {
+        "metric": "cache rows appended/sec (MLA cache write, V3 shape)",
+        "value": round(B / (us * 1e-6), 1), "unit": "rows/s", "n_gpus": 1, "steps": calls, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
+        "config": {"workload": f"V3 cache write, B={B} new tokens, hidden 7168 -> latent 512 + rope 64, bf16 split cache",
+                   "B": B, "D": D, "graph": True, "input_copies_rotated": R},
+        "roofline": {"bound": "hbm", "kernel": "mla_cache_append (%s + k_append_finalize)"
+                                                % ("k_append_gemv" if B <= 8 else "k_append_proj"),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "alg_bytes_per_launch": alg,
+                     "avg_us": round(us, 3)},
+    }
+    if args.cpu_seconds > 0:
+        import threadpoolctl
+        from oracle import decode_bf16
+        from oracle.cache_write import cache_row
+        cores = len(os.sched_getaffinity(0))
+        h, Wd, Wr = decode_bf16(inp.h), decode_bf16(inp.W_DKV), decode_bf16(inp.W_KR)
+        pnp = pos.cpu().numpy()
+        with threadpoolctl.threadpool_limits(limits=cores):
+            info = threadpoolctl.threadpool_info()
+            threads = max([i.get("num_threads", 1) for i in info] or [1])
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds:
+                cache_row(h, Wd, Wr, pnp)
+                n += 1
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n * B / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{n} oracle calls on the same {B} tokens (float64 numpy), {dt:.1f} s"}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

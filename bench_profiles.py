@@ -84,8 +84,11 @@ def cmd_stats(a):
             tail = v[-a.loop:]
             lines.append(f"    {name}: {statistics.mean(e - s_ for s_, e in tail) / 1e3:.2f} us")
     if bench:
-        lines += ["", "bench.py line of the same run (HIP-event averages, us): " + json.dumps(bench["kernels_us"]),
-                  f"ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
+        if "kernels_us" in bench:
+            lines += ["", "bench.py line of the same run (HIP-event averages, us): " + json.dumps(bench["kernels_us"])]
+        else:
+            lines += ["", "bench.py line of the same run:"]
+        lines += [f"ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
                   f"roofline {json.dumps(bench['roofline'])}"]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -10,7 +10,9 @@
 // reads.
 //
 // Two passes:
-//  * k_append_proj: the projection [B x D] . [D x 576] on bf16 MFMA 32x32x16 with fp32
+//  * k_append_gemv (B <= 8): a streaming GEMV over coalesced weight rows, split over D in chunks
+//    of 512 (see below);
+//  * k_append_proj (B > 8): the projection [B x D] . [D x 576] on bf16 MFMA 32x32x16 with fp32
 //    accumulation, split over D in chunks of 512 so that the 8.3 MB of weights stream from many
 //    CUs at once even for one token.  One wave per workgroup computes a 32-token x 32-output tile
 //    of one chunk; both operands come straight from global memory in the MFMA operand layout
@@ -63,6 +65,63 @@ __global__ __launch_bounds__(64) void k_append_proj(const uint16_t* __restrict__
   }
 }
 
+// Few tokens (B <= 8): streaming GEMV.  Grid (576 / 8 row groups, D / 512 chunks), 64 threads.
+// The wave reads rows 8g .. 8g+7 of [W_DKV; W_KR] over one 512-wide chunk (lane l: elements
+// 8l .. 8l+7, so each load is one contiguous KiB of a row) and the matching chunk of every h row,
+// then sums the NB x 8 lane products over the 64 lanes with a halving exchange (each step halves
+// the values a lane holds and doubles the lanes summed into each).
+template <int NB>
+__global__ __launch_bounds__(64) void k_append_gemv(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
+                                                    const uint16_t* __restrict__ w_kr, int B, int D,
+                                                    float* __restrict__ part) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x, ks = blockIdx.y;
+  const int k = ks * kKChunk + 8 * lane;
+  u32x4 wv[8], hv[NB];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int j = 8 * g + r;
+    wv[r] = *(const u32x4*)((j < 512 ? w_dkv + (int64_t)j * D : w_kr + (int64_t)(j - 512) * D) + k);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) hv[b] = *(const u32x4*)(h + (int64_t)min(b, B - 1) * D + k);
+  constexpr int K = NB * 8;   // values per lane before the exchange: index b * 8 + r
+  float v[K];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc = fmaf(__uint_as_float(hv[b][c] << 16), __uint_as_float(wv[r][c] << 16), acc);
+        acc = fmaf(__uint_as_float(hv[b][c] & 0xffff0000u), __uint_as_float(wv[r][c] & 0xffff0000u), acc);
+      }
+      v[b * 8 + r] = acc;
+    }
+  constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : NB == 4 ? 5 : 6;   // log2 K
+#pragma unroll
+  for (int step = 0; step < LK; ++step) {
+    const int d = 32 >> step;
+    const int half = K >> (step + 1);
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? v[i] : v[i + half];
+      const float keep = upper ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, d, 64);
+    }
+  }
+  // after LK steps lane l holds the partial of value index (l >> (6 - LK)) summed over the lanes
+  // that share it; finish over the remaining 64 / K lane bits
+  float t = v[0];
+#pragma unroll
+  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+  const int idx = (lane >> (6 - LK)) & (K - 1);
+  const int b = idx >> 3, r = idx & 7;
+  if ((lane & ((64 >> LK) - 1)) == 0 && b < B) part[((int64_t)ks * B + b) * kOut + 8 * g + r] = t;
+}
+
 namespace {
 // float -> OCP E4M3 code, |y| <= 448 (clamped by the caller), round to nearest even:
 // below 2^-6 the grid step is 2^-9 (subnormals), in [2^e, 2^(e+1)) it is 2^(e-3)
@@ -93,14 +152,23 @@ __global__ __launch_bounds__(256) void k_append_finalize(const float* __restrict
   const int64_t kstride = (int64_t)B * kOut;
   float2 lat = make_float2(0.f, 0.f);
   float2 rp = make_float2(0.f, 0.f);
-  for (int ks = 0; ks < nks; ++ks) {
-    const float2 v = *(const float2*)(p + ks * kstride + 2 * t);
-    lat.x += v.x;
-    lat.y += v.y;
-    if (t < 32) {
-      const float2 r = *(const float2*)(p + ks * kstride + 512 + 2 * t);
-      rp.x += r.x;
-      rp.y += r.y;
+  // chunks in groups of 8: all loads of a group are in flight together, the sums keep chunk order
+  for (int k0 = 0; k0 < nks; k0 += 8) {
+    float2 v[8], r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ks = min(k0 + u, nks - 1);
+      v[u] = *(const float2*)(p + ks * kstride + 2 * t);
+      r[u] = t < 32 ? *(const float2*)(p + ks * kstride + 512 + 2 * t) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u < nks) {
+        lat.x += v[u].x;
+        lat.y += v[u].y;
+        rp.x += r[u].x;
+        rp.y += r[u].y;
+      }
     }
   }
   const int ps = pos[b];
@@ -145,9 +213,20 @@ __global__ __launch_bounds__(256) void k_append_finalize(const float* __restrict
 
 hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
                          const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s) {
-  const dim3 g1(kOut / 32, (B + 31) / 32, D / kKChunk);
-  hipLaunchKernelGGL(k_append_proj, g1, dim3(64), 0, s, (const uint16_t*)h, (const uint16_t*)w_dkv,
-                     (const uint16_t*)w_kr, B, D, ws);
+  if (B <= 8) {
+    const dim3 g0(kOut / 8, D / kKChunk);
+#define MLA_GEMV(NB) hipLaunchKernelGGL(k_append_gemv<NB>, g0, dim3(64), 0, s, (const uint16_t*)h, \
+                                        (const uint16_t*)w_dkv, (const uint16_t*)w_kr, B, D, ws)
+    if (B == 1) MLA_GEMV(1);
+    else if (B == 2) MLA_GEMV(2);
+    else if (B <= 4) MLA_GEMV(4);
+    else MLA_GEMV(8);
+#undef MLA_GEMV
+  } else {
+    const dim3 g1(kOut / 32, (B + 31) / 32, D / kKChunk);
+    hipLaunchKernelGGL(k_append_proj, g1, dim3(64), 0, s, (const uint16_t*)h, (const uint16_t*)w_dkv,
+                       (const uint16_t*)w_kr, B, D, ws);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nks = D / kKChunk;

@@ -67,8 +67,8 @@ def _oracle(inp, pos):
     return cache_row(decode_bf16(inp.h), decode_bf16(inp.W_DKV), decode_bf16(inp.W_KR), np.asarray(pos))
 
 
-@pytest.mark.parametrize("B,N,fp8", [(1, 64, False), (5, 300, False), (40, 8, False), (130, 4, False),
-                                     (5, 300, True), (33, 16, True)])
+@pytest.mark.parametrize("B,N,fp8", [(1, 64, False), (2, 70, False), (5, 300, False), (40, 8, False),
+                                     (130, 4, False), (1, 64, True), (5, 300, True), (33, 16, True)])
 def test_append_split(B, N, fp8):
     from mla_latent_kv_attn_amd.ops import Cache
     inp = make_append_inputs(B, D, seed=100 + B)
@@ -119,14 +119,14 @@ def test_append_packed():
     _check_bf16(g[rows][:, DC:], ref["k_R"], "rope")
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_append_paged(fp8):
+@pytest.mark.parametrize("fp8,B", [(False, 4), (True, 4), (False, 2), (False, 1)])
+def test_append_paged(fp8, B):
     from mla_latent_kv_attn_amd.ops import Cache
-    B, P, pages = 4, 64, 6
+    P, pages = 64, 6
     inp = make_append_inputs(B, D, seed=9)
     rng = np.random.default_rng(3)
     bt = rng.permutation(B * pages).astype(np.int32).reshape(B, pages)
-    pos = np.array([0, 63, 64, 6 * 64 - 1])
+    pos = np.array([6 * 64 - 1, 0, 63, 64])[:B]
     n_pool = B * pages
     if fp8:
         lat0 = np.full((n_pool, P, DC), SENT8, dtype=np.uint8)
