@@ -71,8 +71,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--row", choices=["decode", "append"], default="decode",
-                    help="decode: the absorbed decode step (default); append: the cache write of one step")
+    ap.add_argument("--row", choices=["decode", "append", "mha"], default="decode",
+                    help="decode: the absorbed decode step (default); append: the cache write of one step; "
+                         "mha: the same-dimension MHA decode beside the latent path's attention pass")
     ap.add_argument("--append-batch", type=int, default=1, help="--row append: new tokens (sequences) per call")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
@@ -175,6 +176,9 @@ def main():
 
     if args.row == "append":
         main_append(args)
+        return
+    if args.row == "mha":
+        main_mha(args)
         return
 
     from mla_latent_kv_attn_amd import ops
@@ -407,6 +411,132 @@ def main_append(args):
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def _graph_time_us(fns, steps, stream):
+    """Average time of one call, over a graph holding the calls fns[0..n-1] (one per input copy)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(steps / len(fns)))
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(fns)), reps * len(fns)
+
+
+def main_mha(args):
+    """Same-dimension comparison: plain MHA decode with explicit per-head K/V (keys 192, values 128
+    per head, H = 128) on the lengths of a latent-path workload, timed beside that workload's
+    attention pass (mla_decode_attn: partial + combine, q' and q_R in, o_latent out).  K/V and q are
+    seeded normal bf16 tensors drawn on the device (the MHA cache of the paged 32k workload is 43 GB)."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_attn_amd import ops
+    from workloads import make_inputs
+    from workloads.configs import WORKLOADS
+    from workloads.device import device_cache, to_device
+
+    wl = WORKLOADS[args.config]
+    if wl.dtype != "bf16":
+        raise SystemExit("--row mha compares against a bf16 workload (configs 2-4)")
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    inp = make_inputs(wl, poison=False)
+    lens_np = inp.lens.astype(np.int64)
+    sum_len = int(lens_np.sum())
+    B, H, N = wl.B, wl.H, wl.n_max
+    # ---- MHA: K/V bytes per cached token 2 * H * (192 + 128)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    kv_bytes = B * H * N * (192 + 128) * 2
+    R = max(1, min(4, math.ceil(args.rotate_mb * 1e6 / kv_bytes)))
+    print(f"[bench] MHA caches {kv_bytes / 1e9:.2f} GB x {R}", file=sys.stderr, flush=True)
+    mcopies = []
+    for _ in range(R):
+        K = torch.randn((B, H, N, 192), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        V = torch.randn((B, H, N, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        mcopies.append((K, V))
+    q = torch.randn((B, H, 192), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    lens = torch.from_numpy(inp.lens).to(dev)
+    ws = torch.empty(ops.mla_mha_decode_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
+    mha_fns = [(lambda c=c: ops.mla_mha_decode(q, c[0], c[1], lens, N, workspace=ws, out=out, stream=stream))
+               for c in mcopies]
+    mha_us, calls = _graph_time_us(mha_fns, max(10, args.steps // 10), stream)
+    del mcopies
+    torch.cuda.empty_cache()
+    # ---- the latent path's attention pass on the same lengths
+    base = to_device(inp, dev)
+    per_copy = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    RL = max(1, min(64, math.ceil(args.rotate_mb * 1e6 / per_copy)))
+    copies = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(RL - 1)]
+    caches = [device_cache(inp, c) for c in copies]
+    q_abs = [ops.mla_absorb_q(c["q_C"], c["W_UK"]) for c in copies]
+    mws = torch.empty(ops.mla_decode_workspace_bytes(B, H, wl.d_c, N), dtype=torch.uint8, device=dev)
+    o_lat = torch.empty((B, H, wl.d_c), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(wl.d_h + wl.d_R)
+    mla_fns = [(lambda i=i: ops.mla_decode_attn(q_abs[i], copies[i]["q_R"], caches[i], copies[i]["lens"], N, scale=scale,
+                                                workspace=mws, o_latent=o_lat, want_lse=False,
+                                                stream=stream)) for i in range(RL)]
+    mla_us, _ = _graph_time_us(mla_fns, args.steps, stream)
+    mha_bytes = sum_len * H * (192 + 128) * 2 + B * H * (192 * 2 + 128 * 4)
+    mla_bytes = sum_len * (wl.d_c + wl.d_R) * 2 + B * H * ((wl.d_c + wl.d_R) * 2 + wl.d_c * 4)
+    ach = mha_bytes / (mha_us * 1e-6) / 1e9
+    out_j = {
+        "metric": "cached tokens/sec, same-dimension MHA decode (comparison with the latent path)",
+        "value": round(sum_len / (mha_us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": calls,
+        "warmup": args.warmup, "ms_per_step": round(mha_us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; device-drawn normal K/V and q)",
+        "config": {"workload": f"MHA decode at V3 head sizes (H={H}, keys 192, values 128) on the lengths of "
+                               f"{wl.description}", "B": B, "H": H, "sum_len": sum_len, "graph": True,
+                   "input_copies_rotated": R},
+        "roofline": {"bound": "hbm", "kernel": "mla_mha_decode (k_mha_partial + k_mha_combine)",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "alg_bytes_per_launch": mha_bytes,
+                     "avg_us": round(mha_us, 3)},
+        "latent_path": {"call": "mla_decode_attn (partial + combine)", "us": round(mla_us, 3),
+                        "alg_bytes": mla_bytes, "bytes_ratio_mha_over_mla": round(mha_bytes / mla_bytes, 2),
+                        "time_ratio_mha_over_mla": round(mha_us / mla_us, 2)},
+    }
+    if args.cpu_seconds > 0:
+        import threadpoolctl
+        from oracle import attend
+        cores = len(os.sched_getaffinity(0))
+        L0 = int(inp.lens[0])
+        rng = np.random.default_rng(0)
+        Kh = rng.standard_normal((L0, 192))
+        Vh = rng.standard_normal((L0, 128))
+        qh = rng.standard_normal(192)
+        with threadpoolctl.threadpool_limits(limits=cores):
+            info = threadpoolctl.threadpool_info()
+            threads = max([i.get("num_threads", 1) for i in info] or [1])
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds:
+                attend(Kh, Vh, qh, 1.0 / math.sqrt(192))
+                n += 1
+            dt = time.perf_counter() - t0
+        out_j["cpu_baseline"] = {"value": round(n * L0 / dt, 1), "unit": "tokens/s (one head)", "cores": threads,
+                                 "kind": "oracle", "sample": f"{n} oracle attend calls, one head over {L0} tokens "
+                                                             f"(float64 numpy), {dt:.1f} s"}
+    else:
+        out_j["cpu_baseline"] = None
+    print(json.dumps(out_j), flush=True)
 
 
 def traffic_from_profiles(kname: str, workload: str):

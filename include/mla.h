@@ -262,6 +262,33 @@ int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dty
                      const mla_cache_desc* cache, int B, int D, int d_c, int d_R, float rope_base, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Same-dimension comparison path (not part of the latent path): plain multi-head attention decode
+ * with an explicit per-head K/V cache at the V3 head sizes, keys d_k = 192 (128 content + 64 rope
+ * components), values d_v = 128 -- H (d_k + d_v) values per token and layer against the latent
+ * path's d_c + d_R ("Grouped-query and latent attention", section "Multi-head latent attention
+ * (MLA)"; the pages ask for comparisons at the same dimensions, "DeepSeek MLA: ...", section
+ * "Memory savings do not automatically equal latency savings").
+ *
+ * mla_mha_decode_workspace_bytes: workspace for these sizes (num_splits 0 = the library's choice,
+ * the same one mla_mha_decode makes); 0 for invalid sizes.
+ *
+ * mla_mha_decode: out[b,h] = sum_j a_j V[b,h,j] with a = softmax_j(scale q[b,h] . K[b,h,j]) over
+ * j < seq_lens[b]; lse as for mla_decode_attn.
+ *   q        [B, H, d_k] bf16
+ *   k_cache  [B, H, cap, d_k] bf16, v_cache [B, H, cap, d_v] bf16 (head-major rows)
+ *   seq_lens [B] int32 device, 0 <= len <= max_len <= cap (max_len checked on the host)
+ *   out      [B, H, d_v] float32 (written); lse [B, H] float32 or NULL
+ *   workspace at least mla_mha_decode_workspace_bytes(B, H, max_len, num_splits) bytes, 16-byte
+ *            aligned, any contents; overwritten
+ * Supported: dtype MLA_BF16, d_k == 192, d_v == 128, 16-byte aligned pointers.  fp32 arithmetic.
+ * A sequence with len 0 gives out = 0 and lse = -inf.  Two kernel launches on `stream`.
+ */
+size_t mla_mha_decode_workspace_bytes(int B, int H, int max_len, int num_splits);
+int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, const int32_t* seq_lens,
+                   int max_len, int64_t cap, int B, int H, int d_k, int d_v, float scale, int num_splits,
+                   void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -372,3 +372,43 @@ int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dty
 }
 
 }  // extern "C"
+
+namespace {
+// MHA comparison path: splits per (sequence, head) when the caller passes 0 -- about 1024
+// workgroups over the batch, at most one per two 64-token tiles of the longest sequence
+int mha_auto_splits(int B, int H, int max_len) {
+  const int64_t tiles = ((int64_t)max_len + 63) / 64;
+  int64_t w = std::min<int64_t>((tiles + 1) / 2, (1024 + (int64_t)B * H - 1) / ((int64_t)B * H));
+  return (int)std::max<int64_t>(w, 1);
+}
+}  // namespace
+
+extern "C" {
+
+size_t mla_mha_decode_workspace_bytes(int B, int H, int max_len, int num_splits) {
+  if (B < 1 || H < 1 || max_len < 0 || num_splits < 0) return 0;
+  const int W = num_splits > 0 ? num_splits : mha_auto_splits(B, H, max_len);
+  return mla::mha_ws_bytes(B, H, W);
+}
+
+int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, const int32_t* seq_lens,
+                   int max_len, int64_t cap, int B, int H, int d_k, int d_v, float scale, int num_splits,
+                   void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (B < 0 || H < 1 || d_k < 1 || d_v < 1 || max_len < 0 || num_splits < 0 || cap < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return MLA_ERR_SHAPE;
+  if ((int64_t)max_len > cap) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || d_k != 192 || d_v != 128) return MLA_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MLA_ERR_UNSUPPORTED;
+  const int W = num_splits > 0 ? num_splits : mha_auto_splits(B, H, max_len);
+  if (W > 65535) return MLA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < mla::mha_ws_bytes(B, H, W)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  return hip_status(mla::launch_mha(q, k_cache, v_cache, seq_lens, B, H, cap, scale, W, (float*)workspace, out, lse,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -113,6 +113,9 @@ hipError_t launch_uv_bf16w_generic(const float* o_lat, const void* w, float* out
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s);
 hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s);
 size_t append_ws_bytes(int B, int D);
+size_t mha_ws_bytes(int B, int H, int W);
+hipError_t launch_mha(const void* q, const void* kc, const void* vc, const int32_t* lens, int B, int H, int64_t cap,
+                      float scale, int W, float* ws, float* out, float* lse, hipStream_t s);
 hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
                          const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s);
 

@@ -244,3 +244,31 @@ def mla_cache_append(h: torch.Tensor, W_DKV: torch.Tensor, W_KR: torch.Tensor, p
     check("mla_cache_append", _lib.lib().mla_cache_append(
         h.data_ptr(), W_DKV.data_ptr(), W_KR.data_ptr(), dtype_code(h), pos.data_ptr(), ctypes.byref(cache.desc), B,
         D, d_c, d_R, float(rope_base), workspace.data_ptr(), workspace.numel(), _stream(stream, h)))
+
+
+def mla_mha_decode_workspace_bytes(B: int, H: int, max_len: int, num_splits: int = 0) -> int:
+    return int(_lib.lib().mla_mha_decode_workspace_bytes(B, H, max_len, num_splits))
+
+
+def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                   max_len: int, scale: Optional[float] = None, num_splits: int = 0, workspace=None, out=None,
+                   lse=None, stream=None) -> torch.Tensor:
+    """Same-dimension MHA decode (comparison path): q [B,H,192], k_cache [B,H,cap,192],
+    v_cache [B,H,cap,128] bf16 -> out [B,H,128] float32."""
+    _dev(q, k_cache, v_cache, seq_lens, workspace, out, lse)
+    B, H, d_k = q.shape
+    cap, d_v = k_cache.shape[2], v_cache.shape[3]
+    if not (q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("q, k_cache and v_cache must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(mla_mha_decode_workspace_bytes(B, H, max_len, num_splits), 1), dtype=torch.uint8,
+                                device=q.device)
+    check("mla_mha_decode", _lib.lib().mla_mha_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), dtype_code(q), seq_lens.data_ptr(), int(max_len), cap,
+        B, H, d_k, d_v, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(stream, q)))
+    return out

@@ -208,3 +208,26 @@ def test_cache_append_validation(lib):
     assert call(_desc(latent_dtype=L.MLA_FP8_E4M3)) == L.MLA_ERR_NULL     # fp8 needs the scale
     assert call(_desc(st_tok=577)) == L.MLA_ERR_UNSUPPORTED               # unaligned rows
     assert call(_desc(bt=FAKE, page=0, max_pages=4)) == L.MLA_ERR_SHAPE   # paged without a page size
+
+
+def test_mha_decode_validation(lib):
+    f = lib.mla_mha_decode
+    ws = lib.mla_mha_decode_workspace_bytes
+    assert ws(1, 128, 4096, 0) == 1 * 128 * 8 * 130 * 4     # auto: min(32, ceil(1024/128)) = 8 splits
+    assert ws(2, 8, 300, 3) == 2 * 8 * 3 * 130 * 4 and ws(0, 8, 300, 3) == 0
+
+    def call(B=2, H=8, d_k=192, d_v=128, max_len=300, cap=320, dtype=L.MLA_BF16, scale=0.07, splits=3, wsp=FAKE,
+             wsb=1 << 30, q=FAKE, out=FAKE):
+        return f(q, FAKE, FAKE, dtype, FAKE, max_len, cap, B, H, d_k, d_v, scale, splits, wsp, wsb, out, None, None)
+
+    assert call(B=-1) == L.MLA_ERR_SHAPE
+    assert call(cap=0) == L.MLA_ERR_SHAPE
+    assert call(max_len=321) == L.MLA_ERR_SHAPE             # longer than the cache
+    assert call(scale=-1.0) == L.MLA_ERR_SHAPE
+    assert call(dtype=5) == L.MLA_ERR_DTYPE
+    assert call(B=0, q=None, out=None) == L.MLA_OK
+    assert call(out=None) == L.MLA_ERR_NULL
+    assert call(d_k=128) == L.MLA_ERR_UNSUPPORTED
+    assert call(dtype=L.MLA_F32) == L.MLA_ERR_UNSUPPORTED
+    assert call(q=FAKE + 8) == L.MLA_ERR_UNSUPPORTED
+    assert call(wsb=100) == L.MLA_ERR_WORKSPACE
