@@ -22,6 +22,12 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   cache_write.*    pinned: closed forms and invariants of the cache write (the new
                    token's latent W_DKV h and rotated rope key RoPE_pos(W_KR h), and
                    their bf16 / E4M3 storage forms), tests/test_oracle_cache_write.py.
+  query.*          pinned: basis vectors and head slices of the query projections, single
+                   rotary components per head, the relative-position property against the
+                   cache write's k_R, a hand-computed fold, the fold against explicit keys,
+                   tests/test_oracle_query.py.
+  output.*         pinned: basis vectors of W_O, a hand-computed fold, and the folded product
+                   against W_O of the explicit-value decode, tests/test_oracle_output.py.
   decode_bf16 / decode_e4m3  pinned: OCP FP8 special values, bf16 bit patterns.
   The rotary pairing convention of the input generator is not fixed by the
   pages: parity unpinned for that convention (both sides consume the same
@@ -33,3 +39,5 @@ from .mla_decode import (  # noqa: F401
 )
 from . import cache_size  # noqa: F401
 from . import cache_write  # noqa: F401
+from . import query  # noqa: F401
+from . import output  # noqa: F401
