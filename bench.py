@@ -71,10 +71,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--row", choices=["decode", "append", "mha"], default="decode",
+    ap.add_argument("--row", choices=["decode", "append", "mha", "query", "out"], default="decode",
                     help="decode: the absorbed decode step (default); append: the cache write of one step; "
-                         "mha: the same-dimension MHA decode beside the latent path's attention pass")
-    ap.add_argument("--append-batch", type=int, default=1, help="--row append: new tokens (sequences) per call")
+                         "mha: the same-dimension MHA decode beside the latent path's attention pass; "
+                         "query: the query side (c_q, q_C, q_R, then q' unfolded or through the folded "
+                         "W_UK^T W_UQ); out: the output side (W_UV then W_O, or the folded W_O W_UV)")
+    ap.add_argument("--append-batch", type=int, default=1,
+                    help="--row append / query / out: new tokens (sequences) per call")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
     return ap.parse_args()
@@ -179,6 +182,9 @@ def main():
         return
     if args.row == "mha":
         main_mha(args)
+        return
+    if args.row in ("query", "out"):
+        main_proj(args)
         return
 
     from mla_latent_kv_attn_amd import ops
@@ -408,6 +414,149 @@ def main_append(args):
             dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(n * B / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
                                "sample": f"{n} oracle calls on the same {B} tokens (float64 numpy), {dt:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def main_proj(args):
+    """The projections around the attention core at the V3 shape (hidden 7168, d_q 1536, 128 heads,
+    d_h 128, d_c 512, d_R 64), B new tokens, bf16 weights rotated over enough copies to miss the
+    256 MB Infinity Cache, each call timed in a HIP graph.
+      query: mla_query_proj (c_q = W_DQ h, q_C = W_UQ c_q, q_R = RoPE(W_QR c_q)) then mla_absorb_q
+             (q' = W_UK^T q_C), beside mla_absorb_q_folded (q' = W_QK c_q with the folded weights);
+      out:   mla_uv_out (o = W_UV o_lat) then mla_out_proj (W_O o), beside mla_out_proj with the
+             folded W_OV = W_O W_UV applied to o_lat."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_attn_amd import ops
+    from workloads.proj import make_output_inputs, make_query_inputs
+
+    B = args.append_batch
+    D, d_q, H, d_h, d_c, d_R = 7168, 1536, 128, 128, 512, 64
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def nbytes(ts):
+        return sum(t.numel() * t.element_size() for t in ts)
+
+    def rotated(base):
+        R = max(1, min(64, math.ceil(args.rotate_mb * 1e6 / nbytes(base.values()))))
+        return [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+
+    def timed(copies, call):
+        us, calls = _graph_time_us([lambda c=c: call(c) for c in copies], args.steps, stream)
+        return us, calls
+
+    if args.row == "query":
+        inp = make_query_inputs(B)
+        h, pos = bf16(inp.h), torch.from_numpy(inp.pos).to(dev)
+        c_q = torch.empty(B, d_q, dtype=torch.bfloat16, device=dev)
+        q_C = torch.empty(B, H, d_h, dtype=torch.bfloat16, device=dev)
+        q_R = torch.empty(B, H, d_R, dtype=torch.bfloat16, device=dev)
+        q_abs = torch.empty(B, H, d_c, dtype=torch.bfloat16, device=dev)
+        wsz = max(ops.mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R), ops.mla_proj_workspace_bytes(B, H * d_c, d_q))
+        ws = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+        base = {"W_DQ": bf16(inp.W_DQ), "W_UQ": bf16(inp.W_UQ), "W_QR": bf16(inp.W_QR)}
+        t_proj, calls = timed(rotated(base), lambda c: ops.mla_query_proj(
+            h, c["W_DQ"], c["W_UQ"], c["W_QR"], pos, H, c_q=c_q, q_C=q_C, q_R=q_R, workspace=ws, stream=stream))
+        uk = rotated({"W_UK": bf16(inp.W_UK)})
+        t_abs, _ = timed(uk, lambda c: ops.mla_absorb_q(q_C, c["W_UK"], out=q_abs, stream=stream))
+        W_QK = ops.mla_fold_q(base["W_UQ"], uk[0]["W_UK"])
+        torch.cuda.synchronize()
+        t_fold, _ = timed(rotated({"W_QK": W_QK}), lambda c: ops.mla_absorb_q_folded(
+            c_q, c["W_QK"], out=q_abs, workspace=ws, stream=stream))
+        w_main = nbytes(base.values())
+        alg = w_main + B * D * 2 + B * d_q * 2 * 2 + B * H * (d_h + d_R) * 2 + B * 4
+        achieved = alg / (t_proj * 1e-6) / 1e9
+        step_us = t_proj + t_abs
+        out = {
+            "metric": "query-side tokens/sec (c_q, q_C, q_R and the absorbed q', V3 shape)",
+            "value": round(B / (step_us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": calls,
+            "warmup": args.warmup, "ms_per_step": round(step_us / 1e3, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
+            "config": {"workload": f"V3 query side, B={B} new tokens, hidden 7168 -> c_q 1536 -> 128 x (128 + 64), "
+                                   "then W_UK^T q_C", "B": B, "graph": True},
+            "kernels_us": {"mla_query_proj": round(t_proj, 3), "mla_absorb_q": round(t_abs, 3),
+                           "mla_absorb_q_folded": round(t_fold, 3)},
+            "folded_variant": {"us": round(t_proj + t_fold, 3), "note": "the folded path still needs c_q and q_R "
+                               "(timed here as the whole mla_query_proj); its own weight read is W_QK",
+                               "weight_bytes_unfolded": w_main + H * d_h * d_c * 2,
+                               "weight_bytes_folded": nbytes([base["W_DQ"], base["W_QR"], W_QK])},
+            "roofline": {"bound": "hbm", "kernel": "mla_query_proj (%s)" % ("k_proj_gemv x2" if B <= 8 else
+                                                                           "k_proj_mfma + k_proj_reduce, x2"),
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "alg_bytes_per_launch": alg, "avg_us": round(t_proj, 3)},
+        }
+    else:
+        inp = make_output_inputs(B)
+        o_lat = torch.from_numpy(inp.o_lat).to(dev)
+        o = torch.empty(B, H, d_h, dtype=torch.float32, device=dev)
+        y = torch.empty(B, D, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(ops.mla_proj_workspace_bytes(B, D, H * d_c), 16), dtype=torch.uint8, device=dev)
+        base = {"W_O": bf16(inp.W_O), "W_UV": bf16(inp.W_UV)}
+        copies = rotated(base)
+        t_uv, calls = timed(copies, lambda c: ops.mla_uv_out(o_lat, c["W_UV"], out=o, stream=stream))
+        t_o, _ = timed(copies, lambda c: ops.mla_out_proj(o, c["W_O"], out=y, workspace=ws, stream=stream))
+        W_OV = ops.mla_fold_o(base["W_O"], base["W_UV"])
+        torch.cuda.synchronize()
+        t_fold, _ = timed(rotated({"W_OV": W_OV}), lambda c: ops.mla_out_proj(o_lat, c["W_OV"], out=y, workspace=ws,
+                                                                             stream=stream))
+        alg = nbytes([base["W_O"]]) + B * H * d_h * 4 + B * D * 4
+        achieved = alg / (t_o * 1e-6) / 1e9
+        step_us = t_uv + t_o
+        out = {
+            "metric": "output-side tokens/sec (W_UV then W_O, V3 shape)",
+            "value": round(B / (step_us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": calls,
+            "warmup": args.warmup, "ms_per_step": round(step_us / 1e3, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
+            "config": {"workload": f"V3 output side, B={B} tokens, 128 x 512 latent outputs -> 128 x 128 -> 7168",
+                       "B": B, "graph": True},
+            "kernels_us": {"mla_uv_out": round(t_uv, 3), "mla_out_proj": round(t_o, 3),
+                           "mla_out_proj_folded": round(t_fold, 3)},
+            "folded_variant": {"us": round(t_fold, 3), "weight_bytes_unfolded": nbytes(base.values()),
+                               "weight_bytes_folded": nbytes([W_OV])},
+            "roofline": {"bound": "hbm", "kernel": "mla_out_proj (%s)" % ("k_proj_gemv" if B <= 8 else
+                                                                         "k_proj_mfma + k_proj_reduce"),
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "alg_bytes_per_launch": alg, "avg_us": round(t_o, 3)},
+        }
+    if args.cpu_seconds > 0:
+        import threadpoolctl
+        import oracle.output as oo
+        import oracle.query as oq
+        from oracle import decode_bf16
+        cores = len(os.sched_getaffinity(0))
+        if args.row == "query":
+            Wd, Wu, Wr, Wk = (decode_bf16(x) for x in (inp.W_DQ, inp.W_UQ, inp.W_QR, inp.W_UK))
+            hh = decode_bf16(inp.h)
+
+            def once():
+                qc, _ = oq.q_up(Wu, Wr, oq.q_down(Wd, hh), inp.pos, H)
+                oq.absorb(Wk, qc)
+        else:
+            Wo, Wv = decode_bf16(inp.W_O), decode_bf16(inp.W_UV)
+
+            def once():
+                oo.out_proj(Wo, np.einsum("hik,bhk->bhi", Wv, inp.o_lat.astype(np.float64)))
+        with threadpoolctl.threadpool_limits(limits=cores):
+            info = threadpoolctl.threadpool_info()
+            threads = max([i.get("num_threads", 1) for i in info] or [1])
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds:
+                once()
+                n += 1
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n * B / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{n} oracle passes over the same {B} tokens (float64 numpy), {dt:.1f} s"}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

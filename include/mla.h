@@ -289,6 +289,86 @@ int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int 
                    int max_len, int64_t cap, int B, int H, int d_k, int d_v, float scale, int num_splits,
                    void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
 
+/*
+ * Projections around the attention core.  Each is y[b, n] = sum_k W[n, k] x[b, k] over a bf16
+ * weight W [N, K] (row n maps x to output n, the column-vector form y = W x) with fp32
+ * accumulation.  Up to 8 tokens: a streaming GEMV, no workspace needed.  More tokens: bf16 MFMA
+ * (fp32 x is rounded to bf16 for it) split over K, partial sums in the workspace, added in a
+ * fixed order.  Deterministic.
+ *
+ * mla_proj_workspace_bytes: workspace of one projection with B tokens, N outputs, K inputs
+ * (0 when B <= 8); mla_query_workspace_bytes: workspace of mla_query_proj (the larger of its two
+ * projections).  0 for invalid sizes.
+ */
+size_t mla_proj_workspace_bytes(int B, int N, int K);
+size_t mla_query_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R);
+
+/*
+ * mla_query_proj -- the query side of a decode step ("Grouped-query and latent attention",
+ * sections "Multi-head latent attention (MLA)" and "Why a separate rotary key"):
+ *   c_q = W_DQ h,   q_C = W_UQ c_q,   q_R = RoPE_pos(W_QR c_q) per head
+ *   h     [B, D] bf16            hidden states of the new tokens
+ *   W_DQ  [d_q, D] bf16          W_UQ [H d_h, d_q] bf16 (head h: rows h d_h ..)
+ *   W_QR  [H d_R, d_q] bf16      (head h: rows h d_R ..)
+ *   pos   [B] int32 device       position of each new token (the rotation the cache write gives
+ *                                its key: pair (2i, 2i+1) of each head turned by
+ *                                pos * rope_base^(-2i/d_R), angles in double precision)
+ *   c_q   [B, d_q] bf16 written  (also the input of mla_absorb_q_folded)
+ *   q_C   [B, H, d_h] bf16 written (the input of mla_absorb_q), q_R [B, H, d_R] bf16 written
+ *         (the input of mla_decode_attn)
+ *   workspace at least mla_query_workspace_bytes(...) bytes (NULL allowed when that is 0),
+ *         16-byte aligned, any contents; overwritten
+ * c_q is rounded to bf16 before the second projection reads it.  No normalisation is applied.
+ * Supported: dtype MLA_BF16, d_R == 64, d_h even, D and d_q multiples of 512, d_q and
+ * H (d_h + d_R) multiples of 32, 16-byte aligned pointers.  B == 0 is a no-op.  Two projections
+ * on `stream` (one kernel each up to 8 tokens, two beyond).
+ */
+int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, int dtype,
+                   const int32_t* pos, int B, int D, int d_q, int H, int d_h, int d_R, float rope_base, void* c_q,
+                   void* q_C, void* q_R, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_fold_q -- the absorbed query projection, folded once when the weights are loaded
+ * ("The Journey to Multi-Head Latent Attention", section "The absorption trick (the magic)"):
+ *   W_QK[h] = W_UK[h]^T W_UQ[h d_h : (h+1) d_h, :]      [H, d_c, d_q] bf16 written
+ *   W_UQ [H d_h, d_q] bf16, W_UK [H, d_h, d_c] bf16 (the layout mla_absorb_q takes)
+ * fp32 sums of the exact bf16 products, rounded to bf16 once.  Supported: dtype MLA_BF16, d_h a
+ * multiple of 32, d_c and d_q multiples of 64, 16-byte aligned pointers.  One kernel on `stream`.
+ *
+ * mla_absorb_q_folded -- q'[b, h] = W_QK[h] c_q[b]: the same absorbed query mla_absorb_q makes
+ * from q_C, computed from c_q with the folded weights.
+ *   c_q [B, d_q] bf16, W_QK [H, d_c, d_q] bf16, q_abs [B, H, d_c] written, MLA_BF16 or MLA_F32
+ *   workspace at least mla_proj_workspace_bytes(B, H d_c, d_q) bytes (NULL allowed when 0)
+ * Supported: dtype MLA_BF16, d_q a multiple of 512, H d_c a multiple of 32, 16-byte aligned
+ * pointers.  B == 0 is a no-op.
+ */
+int mla_fold_q(const void* W_UQ, const void* W_UK, int dtype, void* W_QK, int H, int d_h, int d_c, int d_q,
+               void* stream);
+int mla_absorb_q_folded(const void* c_q, const void* W_QK, int dtype, void* q_abs, int out_dtype, int B, int H,
+                        int d_c, int d_q, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_out_proj -- the output projection after the heads ("The Journey to Multi-Head Latent
+ * Attention", section "The absorption trick (the magic)"): out[b] = W x[b] with
+ *   x   [B, K] float32: the heads' outputs o [B, H, d_h] of mla_uv_out (K = H d_h, W = W_O), or
+ *       the latent outputs [B, H, d_c] of mla_decode_attn (K = H d_c, W = W_OV from mla_fold_o)
+ *   W   [D, K] bf16, out [B, D] float32 written
+ *   workspace at least mla_proj_workspace_bytes(B, D, K) bytes (NULL allowed when 0)
+ * Supported: w_dtype MLA_BF16, D a multiple of 32, K a multiple of 512, 16-byte aligned
+ * pointers.  B == 0 is a no-op.
+ *
+ * mla_fold_o -- W_UV merged into W_O once when the weights are loaded ("Grouped-query and latent
+ * attention", section "The absorption trick"):
+ *   W_OV[:, h d_c : (h+1) d_c] = W_O[:, h d_h : (h+1) d_h] W_UV[h]     [D, H d_c] bf16 written
+ *   W_O [D, H d_h] bf16, W_UV [H, d_h, d_c] bf16 (the layout mla_uv_out takes)
+ * fp32 sums, rounded to bf16 once.  Supported: dtype MLA_BF16, d_h a multiple of 32, d_c and D
+ * multiples of 64, 16-byte aligned pointers.  One kernel on `stream`.
+ */
+int mla_out_proj(const float* x, const void* W, int w_dtype, float* out, int B, int D, int K, void* workspace,
+                 size_t workspace_bytes, void* stream);
+int mla_fold_o(const void* W_O, const void* W_UV, int dtype, void* W_OV, int D, int H, int d_h, int d_c,
+               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ ARCH = "gfx950"
 
 SOURCES = ["mla_abi.hip", "decode_generic.hip", "absorb_uv_mfma.hip", "decode_partial_mfma.hip",
            "decode_partial_small.hip", "cache_append.hip",
-           "mha_decode.hip"]
+           "mha_decode.hip", "proj.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -412,3 +412,164 @@ int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// Projections around the attention core: the query side, the folded absorbed query projection,
+// the output projection (and the offline folds that produce the folded weights).
+// ------------------------------------------------------------------------------------------------
+namespace {
+bool proj_shape_ok(int N, int K) { return N >= 32 && (N % 32) == 0 && K >= 512 && (K % 512) == 0; }
+
+mla::ProjArgs proj_args(const void* w0, const void* w1, int n_split, const void* x, int B, int N, int K) {
+  mla::ProjArgs a{};
+  a.w0 = (const uint16_t*)w0;
+  a.w1 = (const uint16_t*)w1;
+  a.n_split = n_split;
+  a.ldw = K;
+  a.x = x;
+  a.ldx = K;
+  a.B = B;
+  a.N = N;
+  a.K = K;
+  a.scale = 1.f;
+  return a;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mla_proj_workspace_bytes(int B, int N, int K) {
+  if (B < 1 || N < 1 || K < 1) return 0;
+  return mla::proj_ws_bytes(B, N, K);
+}
+
+size_t mla_query_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R) {
+  if (B < 1 || D < 1 || d_q < 1 || H < 1 || d_h < 1 || d_R < 1) return 0;
+  const size_t a = mla::proj_ws_bytes(B, d_q, D);
+  const size_t b = mla::proj_ws_bytes(B, H * (d_h + d_R), d_q);
+  return a > b ? a : b;
+}
+
+int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, int dtype,
+                   const int32_t* pos, int B, int D, int d_q, int H, int d_h, int d_R, float rope_base, void* c_q,
+                   void* q_C, void* q_R, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || D < 1 || d_q < 1 || H < 1 || d_h < 1 || d_R < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(rope_base) || !(rope_base > 0.f)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!h || !W_DQ || !W_UQ || !W_QR || !pos || !c_q || !q_C || !q_R) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  const int64_t n2 = (int64_t)H * (d_h + d_R);
+  if (d_R != 64 || (d_h % 2) != 0 || !proj_shape_ok(d_q, D) || n2 > (1 << 30) || !proj_shape_ok((int)n2, d_q))
+    return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(h) || !aligned16(W_DQ) || !aligned16(W_UQ) || !aligned16(W_QR) || !aligned16(c_q) ||
+      !aligned16(q_C) || !aligned16(q_R))
+    return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R);
+  if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  // c_q = W_DQ h, bf16
+  mla::ProjArgs a = proj_args(W_DQ, W_DQ, d_q, h, B, d_q, D);
+  a.y = c_q;
+  a.ldy = d_q;
+  hipError_t e = mla::launch_proj(a, false, true, (float*)workspace, s);
+  if (e != hipSuccess) return hip_status(e);
+  // [q_C ; q_R] = [W_UQ ; W_QR] c_q, the q_R rows rotated at pos
+  mla::ProjArgs u = proj_args(W_UQ, W_QR, H * d_h, c_q, B, (int)n2, d_q);
+  u.y = q_C;
+  u.ldy = (int64_t)H * d_h;
+  u.y1 = q_R;
+  u.ldy1 = (int64_t)H * d_R;
+  u.pos = pos;
+  u.rope_base = rope_base;
+  return hip_status(mla::launch_proj(u, false, true, (float*)workspace, s));
+}
+
+int mla_absorb_q_folded(const void* c_q, const void* W_QK, int dtype, void* q_abs, int out_dtype, int B, int H,
+                        int d_c, int d_q, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 1 || d_c < 1 || d_q < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype) || !known_dtype(out_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!c_q || !W_QK || !q_abs) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || !(out_dtype == MLA_BF16 || out_dtype == MLA_F32)) return MLA_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)H * d_c;
+  if (n > (1 << 30) || !proj_shape_ok((int)n, d_q)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(c_q) || !aligned16(W_QK) || !aligned16(q_abs)) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::proj_ws_bytes(B, (int)n, d_q);
+  if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  mla::ProjArgs a = proj_args(W_QK, W_QK, (int)n, c_q, B, (int)n, d_q);
+  a.y = q_abs;
+  a.ldy = n;
+  return hip_status(mla::launch_proj(a, false, out_dtype == MLA_BF16, (float*)workspace, (hipStream_t)stream));
+}
+
+int mla_out_proj(const float* x, const void* W, int w_dtype, float* out, int B, int D, int K, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (B < 0 || D < 1 || K < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(w_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!x || !W || !out) return MLA_ERR_NULL;
+  if (w_dtype != MLA_BF16 || !proj_shape_ok(D, K)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(out)) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::proj_ws_bytes(B, D, K);
+  if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  mla::ProjArgs a = proj_args(W, W, D, x, B, D, K);
+  a.y = out;
+  a.ldy = D;
+  return hip_status(mla::launch_proj(a, true, false, (float*)workspace, (hipStream_t)stream));
+}
+
+int mla_fold_q(const void* W_UQ, const void* W_UK, int dtype, void* W_QK, int H, int d_h, int d_c, int d_q,
+               void* stream) {
+  if (H < 1 || d_h < 1 || d_c < 1 || d_q < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!W_UQ || !W_UK || !W_QK) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || (d_h % 32) != 0 || (d_c % 64) != 0 || (d_q % 64) != 0 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(W_UQ) || !aligned16(W_UK) || !aligned16(W_QK)) return MLA_ERR_UNSUPPORTED;
+  mla::FoldArgs f{};
+  f.A = (const uint16_t*)W_UK;           // A_h[m = k, i] = W_UK[h, i, k]
+  f.a_sh = (int64_t)d_h * d_c;
+  f.a_sm = 1;
+  f.a_si = d_c;
+  f.B = (const uint16_t*)W_UQ;           // B_h[i, n] = W_UQ[h d_h + i, n]
+  f.b_sh = (int64_t)d_h * d_q;
+  f.b_si = d_q;
+  f.C = (uint16_t*)W_QK;                 // W_QK[h, k, n]
+  f.c_sh = (int64_t)d_c * d_q;
+  f.c_sm = d_q;
+  f.H = H;
+  f.M = d_c;
+  f.Nc = d_q;
+  f.inner = d_h;
+  return hip_status(mla::launch_fold(f, (hipStream_t)stream));
+}
+
+int mla_fold_o(const void* W_O, const void* W_UV, int dtype, void* W_OV, int D, int H, int d_h, int d_c,
+               void* stream) {
+  if (D < 1 || H < 1 || d_h < 1 || d_c < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!W_O || !W_UV || !W_OV) return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || (d_h % 32) != 0 || (d_c % 64) != 0 || (D % 64) != 0 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(W_O) || !aligned16(W_UV) || !aligned16(W_OV)) return MLA_ERR_UNSUPPORTED;
+  mla::FoldArgs f{};
+  f.A = (const uint16_t*)W_O;            // A_h[m, i] = W_O[m, h d_h + i]
+  f.a_sh = d_h;
+  f.a_sm = (int64_t)H * d_h;
+  f.a_si = 1;
+  f.B = (const uint16_t*)W_UV;           // B_h[i, n] = W_UV[h, i, n]
+  f.b_sh = (int64_t)d_h * d_c;
+  f.b_si = d_c;
+  f.C = (uint16_t*)W_OV;                 // W_OV[m, h d_c + n]
+  f.c_sh = d_c;
+  f.c_sm = (int64_t)H * d_c;
+  f.H = H;
+  f.M = D;
+  f.Nc = d_c;
+  f.inner = d_h;
+  return hip_status(mla::launch_fold(f, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -98,6 +98,47 @@ inline size_t ws_prefix_off(int W, int B, int H, int d_c) { return ws_ml_off(W, 
 inline size_t ws_cnt_off(int W, int B, int H, int d_c) { return ws_prefix_off(W, B, H, d_c) + ws_prefix_bytes(B); }
 inline size_t ws_uv_off(int W, int B, int H, int d_c) { return ws_cnt_off(W, B, H, d_c) + ws_cnt_bytes(H); }
 
+// projections y[b, n] = sum_k W[n, k] x[b, k] (proj.hip).  Rows n < n_split come from w0 and are
+// scaled and stored to y; rows n >= n_split come from w1 (row n - n_split) and are the rotary rows,
+// turned per 64-row head block at pos[b] and stored to y1 as bf16.  N % 32 == 0, K % 512 == 0.
+constexpr int kProjGemvMaxB = 8;   // up to this many tokens: the GEMV kernel (no workspace)
+struct ProjArgs {
+  const uint16_t* w0;
+  const uint16_t* w1;
+  int n_split;
+  int64_t ldw;                  // row stride of w0 and w1 (elements)
+  const void* x;                // [B, K] bf16 or fp32, row stride ldx
+  int64_t ldx;
+  int B, N, K;
+  float scale;                  // applied to rows below n_split
+  void* y;                      // [B, n_split] (row stride ldy), bf16 or fp32
+  int64_t ldy;
+  void* y1;                     // [B, N - n_split] bf16 (row stride ldy1), the rotated rows
+  int64_t ldy1;
+  const int32_t* pos;           // [B] positions of the rotary rows
+  float rope_base;
+};
+// MFMA path: K is split into chunks of kc = a multiple of 256 dividing K, at most 2048
+inline int proj_chunks(int K) {
+  const int units = K / 256;
+  int best = 1;
+  for (int u = 1; u <= 8; ++u)
+    if (units % u == 0) best = u;
+  return units / best;
+}
+size_t proj_ws_bytes(int B, int N, int K);
+
+// per-head weight fold C_h[m, n] = sum_{i < inner} A_h[m, i] B_h[i, n] (bf16 in, fp32 sums, bf16 out)
+struct FoldArgs {
+  const uint16_t* A;
+  int64_t a_sh, a_sm, a_si;
+  const uint16_t* B;
+  int64_t b_sh, b_si;           // column stride 1
+  uint16_t* C;
+  int64_t c_sh, c_sm;           // column stride 1
+  int H, M, Nc, inner;          // M % 64 == 0, Nc % 64 == 0, inner % 32 == 0
+};
+
 // launchers (return the launch error; host-side validation happens in mla_abi.cpp)
 hipError_t launch_absorb_f32(const float* q, const float* w, float* out, int B, int H, int d_h, int d_c,
                              hipStream_t s);
@@ -116,6 +157,8 @@ size_t append_ws_bytes(int B, int D);
 size_t mha_ws_bytes(int B, int H, int W);
 hipError_t launch_mha(const void* q, const void* kc, const void* vc, const int32_t* lens, int B, int H, int64_t cap,
                       float scale, int W, float* ws, float* out, float* lse, hipStream_t s);
+hipError_t launch_proj(const ProjArgs& a, bool x_f32, bool y_bf16, float* ws, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& f, hipStream_t s);
 hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
                          const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s);
 

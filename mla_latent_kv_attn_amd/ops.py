@@ -246,6 +246,125 @@ def mla_cache_append(h: torch.Tensor, W_DKV: torch.Tensor, W_KR: torch.Tensor, p
         D, d_c, d_R, float(rope_base), workspace.data_ptr(), workspace.numel(), _stream(stream, h)))
 
 
+def mla_proj_workspace_bytes(B: int, N: int, K: int) -> int:
+    return int(_lib.lib().mla_proj_workspace_bytes(B, N, K))
+
+
+def mla_query_workspace_bytes(B: int, D: int, d_q: int, H: int, d_h: int, d_R: int) -> int:
+    return int(_lib.lib().mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R))
+
+
+def _contig(**ts):
+    for name, t in ts.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _ws(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
+    """(address, size) of the workspace: the caller's, else a fresh one of nbytes (none when 0).
+    A fresh one stays referenced until the next call on the device allocates another."""
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if nbytes == 0:
+        return 0, 0
+    w = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    _WS_HOLD[like.device] = w
+    return w.data_ptr(), nbytes
+
+
+_WS_HOLD = {}
+
+
+def mla_query_proj(h: torch.Tensor, W_DQ: torch.Tensor, W_UQ: torch.Tensor, W_QR: torch.Tensor, pos: torch.Tensor,
+                   H: int, rope_base: float = 10000.0, c_q: Optional[torch.Tensor] = None,
+                   q_C: Optional[torch.Tensor] = None, q_R: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """c_q = W_DQ h, q_C = W_UQ c_q, q_R = RoPE_pos(W_QR c_q) per head.  h [B, D] bf16,
+    W_DQ [d_q, D], W_UQ [H d_h, d_q], W_QR [H d_R, d_q] bf16, pos [B] int32.
+    Returns (c_q [B, d_q], q_C [B, H, d_h], q_R [B, H, d_R]), all bf16."""
+    _dev(h, W_DQ, W_UQ, W_QR, pos, c_q, q_C, q_R, workspace)
+    _contig(h=h, W_DQ=W_DQ, W_UQ=W_UQ, W_QR=W_QR, pos=pos, c_q=c_q, q_C=q_C, q_R=q_R)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos is int32")
+    B, D = h.shape
+    d_q = W_DQ.shape[0]
+    d_h, d_R = W_UQ.shape[0] // H, W_QR.shape[0] // H
+    if c_q is None:
+        c_q = torch.empty(B, d_q, dtype=torch.bfloat16, device=h.device)
+    if q_C is None:
+        q_C = torch.empty(B, H, d_h, dtype=torch.bfloat16, device=h.device)
+    if q_R is None:
+        q_R = torch.empty(B, H, d_R, dtype=torch.bfloat16, device=h.device)
+    wp, wn = _ws(mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R), h, workspace)
+    check("mla_query_proj", _lib.lib().mla_query_proj(
+        h.data_ptr(), W_DQ.data_ptr(), W_UQ.data_ptr(), W_QR.data_ptr(), dtype_code(h), pos.data_ptr(), B, D, d_q,
+        H, d_h, d_R, float(rope_base), c_q.data_ptr(), q_C.data_ptr(), q_R.data_ptr(), wp, wn, _stream(stream, h)))
+    return c_q, q_C, q_R
+
+
+def mla_fold_q(W_UQ: torch.Tensor, W_UK: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """W_QK[h] = W_UK[h]^T W_UQ[h d_h:(h+1) d_h]: W_UQ [H d_h, d_q], W_UK [H, d_h, d_c] -> [H, d_c, d_q] bf16."""
+    _dev(W_UQ, W_UK, out)
+    _contig(W_UQ=W_UQ, W_UK=W_UK, out=out)
+    H, d_h, d_c = W_UK.shape
+    d_q = W_UQ.shape[1]
+    if out is None:
+        out = torch.empty(H, d_c, d_q, dtype=torch.bfloat16, device=W_UK.device)
+    check("mla_fold_q", _lib.lib().mla_fold_q(W_UQ.data_ptr(), W_UK.data_ptr(), dtype_code(W_UK), out.data_ptr(),
+                                              H, d_h, d_c, d_q, _stream(stream, W_UK)))
+    return out
+
+
+def mla_absorb_q_folded(c_q: torch.Tensor, W_QK: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None, stream=None):
+    """q'[b, h] = W_QK[h] c_q[b]: c_q [B, d_q] bf16, W_QK [H, d_c, d_q] bf16 -> [B, H, d_c]."""
+    _dev(c_q, W_QK, out, workspace)
+    _contig(c_q=c_q, W_QK=W_QK, out=out)
+    B, d_q = c_q.shape
+    H, d_c = W_QK.shape[0], W_QK.shape[1]
+    if out is None:
+        out = torch.empty(B, H, d_c, dtype=out_dtype, device=c_q.device)
+    wp, wn = _ws(mla_proj_workspace_bytes(B, H * d_c, d_q), c_q, workspace)
+    check("mla_absorb_q_folded", _lib.lib().mla_absorb_q_folded(
+        c_q.data_ptr(), W_QK.data_ptr(), dtype_code(c_q), out.data_ptr(), dtype_code(out), B, H, d_c, d_q, wp, wn,
+        _stream(stream, c_q)))
+    return out
+
+
+def mla_out_proj(x: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """out[b] = W x[b]: x [B, ...] float32 (flattened to [B, K]), W [D, K] bf16 -> [B, D] float32."""
+    _dev(x, W, out, workspace)
+    _contig(x=x, W=W, out=out)
+    if x.dtype != torch.float32:
+        raise TypeError("x is float32")
+    B = x.shape[0]
+    K = x.numel() // max(B, 1)
+    D = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W has {W.shape[1]} columns, x has {K} values per token")
+    if out is None:
+        out = torch.empty(B, D, dtype=torch.float32, device=x.device)
+    wp, wn = _ws(mla_proj_workspace_bytes(B, D, K), x, workspace)
+    check("mla_out_proj", _lib.lib().mla_out_proj(x.data_ptr(), W.data_ptr(), dtype_code(W), out.data_ptr(), B, D,
+                                                  K, wp, wn, _stream(stream, x)))
+    return out
+
+
+def mla_fold_o(W_O: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """W_OV[:, h d_c:(h+1) d_c] = W_O[:, h d_h:(h+1) d_h] W_UV[h]: W_O [D, H d_h], W_UV [H, d_h, d_c]
+    -> [D, H d_c] bf16."""
+    _dev(W_O, W_UV, out)
+    _contig(W_O=W_O, W_UV=W_UV, out=out)
+    H, d_h, d_c = W_UV.shape
+    D = W_O.shape[0]
+    if out is None:
+        out = torch.empty(D, H * d_c, dtype=torch.bfloat16, device=W_O.device)
+    check("mla_fold_o", _lib.lib().mla_fold_o(W_O.data_ptr(), W_UV.data_ptr(), dtype_code(W_O), out.data_ptr(), D,
+                                              H, d_h, d_c, _stream(stream, W_O)))
+    return out
+
+
 def mla_mha_decode_workspace_bytes(B: int, H: int, max_len: int, num_splits: int = 0) -> int:
     return int(_lib.lib().mla_mha_decode_workspace_bytes(B, H, max_len, num_splits))
 

@@ -231,3 +231,61 @@ def test_mha_decode_validation(lib):
     assert call(dtype=L.MLA_F32) == L.MLA_ERR_UNSUPPORTED
     assert call(q=FAKE + 8) == L.MLA_ERR_UNSUPPORTED
     assert call(wsb=100) == L.MLA_ERR_WORKSPACE
+
+
+def test_projection_workspace_rules(lib):
+    ws = lib.mla_proj_workspace_bytes
+    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0                # GEMV: none
+    # MFMA path: K split into chunks of a multiple of 256 elements, at most 2048, dividing K
+    assert ws(9, 1536, 7168) == 4 * 9 * 1536 * 4                              # 7168 = 4 x 1792
+    assert ws(64, 24576, 1536) == 1 * 64 * 24576 * 4
+    assert ws(128, 7168, 16384) == 8 * 128 * 7168 * 4
+    assert ws(0, 32, 512) == 0
+    q = lib.mla_query_workspace_bytes
+    assert q(1, 7168, 1536, 128, 128, 64) == 0
+    assert q(64, 7168, 1536, 128, 128, 64) == max(ws(64, 1536, 7168), ws(64, 128 * 192, 1536))
+
+
+def test_query_proj_validation(lib):
+    f = lib.mla_query_proj
+
+    def call(B=1, D=7168, d_q=1536, H=128, d_h=128, d_R=64, base=1e4, dtype=L.MLA_BF16, h=FAKE, pos=FAKE,
+             out=FAKE, wsp=None, wsb=0):
+        return f(h, FAKE, FAKE, FAKE, dtype, pos, B, D, d_q, H, d_h, d_R, base, out, FAKE, FAKE, wsp, wsb, None)
+
+    assert call(B=-1) == L.MLA_ERR_SHAPE
+    assert call(base=-1.0) == L.MLA_ERR_SHAPE
+    assert call(dtype=9) == L.MLA_ERR_DTYPE
+    assert call(B=0, h=None, pos=None) == L.MLA_OK
+    assert call(pos=None) == L.MLA_ERR_NULL
+    assert call(out=None) == L.MLA_ERR_NULL
+    assert call(dtype=L.MLA_F32) == L.MLA_ERR_UNSUPPORTED
+    assert call(d_R=32) == L.MLA_ERR_UNSUPPORTED
+    assert call(D=7000) == L.MLA_ERR_UNSUPPORTED
+    assert call(d_q=1000) == L.MLA_ERR_UNSUPPORTED
+    assert call(h=FAKE + 2) == L.MLA_ERR_UNSUPPORTED
+    need = lib.mla_query_workspace_bytes(64, 7168, 1536, 128, 128, 64)
+    assert call(B=64) == L.MLA_ERR_WORKSPACE
+    assert call(B=64, wsp=FAKE, wsb=need - 1) == L.MLA_ERR_WORKSPACE
+    assert call(B=64, wsp=FAKE + 8, wsb=need) == L.MLA_ERR_UNSUPPORTED
+
+
+def test_fold_and_out_proj_validation(lib):
+    fq, fo, ab, op = lib.mla_fold_q, lib.mla_fold_o, lib.mla_absorb_q_folded, lib.mla_out_proj
+    assert fq(FAKE, FAKE, L.MLA_BF16, FAKE, 0, 128, 512, 1536, None) == L.MLA_ERR_SHAPE
+    assert fq(FAKE, FAKE, 7, FAKE, 128, 128, 512, 1536, None) == L.MLA_ERR_DTYPE
+    assert fq(None, FAKE, L.MLA_BF16, FAKE, 128, 128, 512, 1536, None) == L.MLA_ERR_NULL
+    assert fq(FAKE, FAKE, L.MLA_F32, FAKE, 128, 128, 512, 1536, None) == L.MLA_ERR_UNSUPPORTED
+    assert fq(FAKE, FAKE, L.MLA_BF16, FAKE, 128, 100, 512, 1536, None) == L.MLA_ERR_UNSUPPORTED
+    assert fo(FAKE, FAKE, L.MLA_BF16, FAKE, 7000, 128, 128, 512, None) == L.MLA_ERR_UNSUPPORTED
+    assert fo(FAKE, FAKE, L.MLA_BF16, None, 7168, 128, 128, 512, None) == L.MLA_ERR_NULL
+    assert ab(FAKE, FAKE, L.MLA_BF16, FAKE, L.MLA_BF16, 0, 128, 512, 1536, None, 0, None) == L.MLA_OK
+    assert ab(FAKE, FAKE, L.MLA_BF16, FAKE, L.MLA_FP8_E4M3, 1, 128, 512, 1536, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert ab(FAKE, FAKE, L.MLA_BF16, FAKE, L.MLA_BF16, 1, 128, 512, 1000, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert ab(FAKE, FAKE, L.MLA_BF16, FAKE, L.MLA_BF16, 16, 128, 512, 1536, None, 0, None) == L.MLA_ERR_WORKSPACE
+    assert op(FAKE, FAKE, L.MLA_BF16, FAKE, -1, 7168, 16384, None, 0, None) == L.MLA_ERR_SHAPE
+    assert op(FAKE, FAKE, L.MLA_F32, FAKE, 1, 7168, 16384, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 1, 7000, 16384, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 1, 7168, 16000, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert op(FAKE + 4, FAKE, L.MLA_BF16, FAKE, 1, 7168, 16384, None, 0, None) == L.MLA_ERR_UNSUPPORTED
+    assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 9, 7168, 16384, None, 0, None) == L.MLA_ERR_WORKSPACE
