@@ -69,7 +69,22 @@ def cmd_stats(a):
         lines.append(f"| {short} | {_col(r, 'Calls')} | {float(_col(r, 'AverageNs')) / 1e3:.2f} | "
                      f"{float(_col(r, 'MinNs')) / 1e3:.2f} | {float(_col(r, 'MaxNs')) / 1e3:.2f} | "
                      f"{float(_col(r, 'Percentage')):.1f} |")
-    if a.trace and bench:
+    if a.trace and a.by_grid:
+        # one kernel serves several shapes: split its dispatches by launch grid
+        grp = {}
+        for r in _rows(a.trace):
+            name = _col(r, "Kernel_Name").split("(")[0].replace("void ", "")
+            if not name.startswith("mla::"):
+                continue
+            grid = "x".join(str(int(_col(r, f"Grid_Size_{d}")) // max(1, int(_col(r, f"Workgroup_Size_{d}"))))
+                            for d in "XYZ")
+            grp.setdefault((name, grid), []).append(
+                (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3)
+        lines += ["", "Dispatches by launch grid (workgroups x, y, z):", "",
+                  "| kernel | grid | calls | avg us | median us |", "|---|---|---|---|---|"]
+        for (name, grid), v in grp.items():
+            lines.append(f"| {name} | {grid} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} |")
+    if a.trace and bench and not a.by_grid:
         # the bench's per-kernel timing loop is the last kernel_reps dispatches of each kernel
         disp = {}
         for r in _rows(a.trace):
@@ -136,6 +151,7 @@ def main():
     s.add_argument("--out", required=True)
     s.add_argument("--trace", default=None, help="kernel_trace.csv of the same run")
     s.add_argument("--loop", type=int, default=50, help="dispatches per kernel in the bench's timing loop")
+    s.add_argument("--by-grid", action="store_true", help="split each kernel's dispatches by launch grid")
     p = sub.add_parser("pmc")
     p.add_argument("--kernel", required=True)
     p.add_argument("--workload", required=True)

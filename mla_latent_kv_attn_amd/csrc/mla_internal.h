@@ -118,13 +118,15 @@ struct ProjArgs {
   const int32_t* pos;           // [B] positions of the rotary rows
   float rope_base;
 };
-// MFMA path: K is split into chunks of kc = a multiple of 256 dividing K, at most 2048
-inline int proj_chunks(int K) {
+// MFMA path (B > kProjGemvMaxB): workgroup tiles of 128 rows x up to 128 tokens; K is split into
+// proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups
+constexpr int kProjRows = 128, kProjToks = 128;
+inline int proj_chunks(int B, int N, int K) {
+  const int64_t blocks = (int64_t)((N + kProjRows - 1) / kProjRows) * ((B + kProjToks - 1) / kProjToks);
   const int units = K / 256;
-  int best = 1;
-  for (int u = 1; u <= 8; ++u)
-    if (units % u == 0) best = u;
-  return units / best;
+  for (int d = 1; d <= units; ++d)
+    if (units % d == 0 && blocks * d >= 512) return d;
+  return units;
 }
 size_t proj_ws_bytes(int B, int N, int K);
 

@@ -10,16 +10,18 @@
 //
 // For the few tokens of a decode step every weight byte is used B times, so the work is a
 // stream of the weights from HBM.  Two kernels:
-//  * k_proj_gemv (B <= 8): one workgroup (4 waves) per 8 rows of W over the whole of K.  K is
-//    cut into 512-element chunks; wave w takes chunks w, w + 4, ...  Lane l reads elements
-//    8l .. 8l+7 of a chunk of each of the 8 rows (every load instruction is one contiguous KiB of
-//    a row) and of each token's x, keeps 8 x NB fp32 products-sums, and the sums are reduced
-//    over the 64 lanes (halving exchange) and then over the 4 waves through LDS.  No workspace.
-//  * k_proj_mfma (B > 8): bf16 MFMA 32x32x16 with fp32 accumulation on 32-token x 32-row tiles,
-//    split over K in chunks (grid z) so that a few rows still spread over many CUs; operands
-//    come straight from global memory in the MFMA operand layout (16 contiguous bytes of a row
-//    per lane); fp32 x is rounded to bf16 for the MFMA.  The chunks' partial sums go to the
-//    workspace [chunk][token][N] and k_proj_reduce adds them in chunk order.
+//  * k_proj_gemv (B <= 8): one workgroup (4 waves) per R rows of W (R = 2, 4 or 8 by batch) over
+//    the whole of K.  K is cut into 512-element chunks; wave w takes chunks w, w + 4, ... with U
+//    chunks' loads in flight together.  Lane l reads elements 8l .. 8l+7 of a chunk of each of the
+//    R rows (every load instruction is one contiguous KiB of a row) and of each token's x, keeps
+//    R x NB fp32 product sums, and the sums are reduced over the 64 lanes (halving exchange) and
+//    then over the 4 waves through LDS.  No workspace.
+//  * k_proj_mfma (B > 8): bf16 MFMA 32x32x16 with fp32 accumulation on tiles of 128 rows x up
+//    to 128 tokens (4 waves of 32 rows), split over K in chunks (grid z) so that the weights
+//    stream from many CUs at once; x (fp32 rounded to bf16) is staged once per workgroup through
+//    LDS, W comes straight from global memory in the MFMA operand layout (16 contiguous bytes of
+//    a row per lane).  The chunks' partial sums go to the workspace [chunk][token][N] and
+//    k_proj_reduce adds them in chunk order.
 // Both end in the same epilogue on pairs of adjacent outputs (n, n + 1), n even: rows below
 // n_split are scaled and stored to y (bf16 or fp32); rows from n_split on are the rotary rows
 // (pairs (2i, 2i+1) of each 64-row head block turned by pos[b] * base^(-2i/64), angle and its
@@ -39,9 +41,19 @@ constexpr int kRot = 64;           // rotary rows per head block
 __device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// the epilogue of one output pair (n, n + 1) of token b
+// rotation of the rotary pair that holds output n (n >= n_split) of token b: cos and sin of
+// pos[b] * base^(-2i/64), i the pair index within the head, in double precision
+__device__ __forceinline__ float2 rope_cs(const ProjArgs& a, int b, int n) {
+  const int i = ((n - a.n_split) % kRot) >> 1;
+  const double th = (double)a.pos[b] * pow((double)a.rope_base, -2.0 * i / (double)kRot);
+  double sn, cs;
+  sincos(th, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
+// the epilogue of one output pair (n, n + 1) of token b; cs is the pair's rotation when n >= n_split
 template <bool YBF16>
-__device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, float v0, float v1) {
+__device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, float v0, float v1, float2 cs) {
   if (n < a.n_split) {
     v0 *= a.scale;
     v1 *= a.scale;
@@ -50,15 +62,12 @@ __device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, floa
     else
       *(float2*)((float*)a.y + (int64_t)b * a.ldy + n) = make_float2(v0, v1);
   } else {
-    const int n1 = n - a.n_split;
-    const int i = (n1 % kRot) >> 1;                                  // pair index within the head
-    const double th = (double)a.pos[b] * pow((double)a.rope_base, -2.0 * i / (double)kRot);
-    double sn, cs;
-    sincos(th, &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    *(uint32_t*)((uint16_t*)a.y1 + (int64_t)b * a.ldy1 + n1) = pack_bf16x2(v0 * c - v1 * s, v0 * s + v1 * c);
+    *(uint32_t*)((uint16_t*)a.y1 + (int64_t)b * a.ldy1 + (n - a.n_split)) =
+        pack_bf16x2(v0 * cs.x - v1 * cs.y, v0 * cs.y + v1 * cs.x);
   }
 }
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 
 __device__ __forceinline__ const uint16_t* wrow(const ProjArgs& a, int n) {
   return n < a.n_split ? a.w0 + (int64_t)n * a.ldw : a.w1 + (int64_t)(n - a.n_split) * a.ldw;
@@ -81,38 +90,46 @@ __device__ __forceinline__ u32x4 load_x_bf16(const ProjArgs& a, int b, int k) {
 
 size_t proj_ws_bytes(int B, int N, int K) {
   if (B <= kProjGemvMaxB) return 0;
-  return (size_t)proj_chunks(K) * (size_t)B * (size_t)N * sizeof(float);
+  return (size_t)proj_chunks(B, N, K) * (size_t)B * (size_t)N * sizeof(float);
 }
 
 // ------------------------------------------------------------------------------------------------
-// GEMV, B <= 8.  grid (N / 8), 256 threads.
+// GEMV, B <= 8.  grid (N / R), 256 threads; R rows per workgroup.
 // ------------------------------------------------------------------------------------------------
-template <int NB, bool XF32, bool YBF16>
+template <int NB, int R, int U, bool XF32, bool YBF16>
 __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
-  constexpr int U = NB <= 2 ? 4 : (NB == 8 && XF32) ? 1 : 2;   // chunks whose loads are in flight together
   constexpr int XV = XF32 ? 8 : 4;            // x registers per token and chunk
-  __shared__ float red[4][NB * 8];
+  constexpr int KV = NB * R;                  // lane partial sums
+  constexpr int LK = ilog2(KV);
+  static_assert((KV & (KV - 1)) == 0 && KV >= 2 && KV <= 64, "NB x R: a power of two in [2, 64]");
+  __shared__ float red[4][KV];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int n0 = 8 * blockIdx.x;
+  const int n0 = R * blockIdx.x;
   const int nch = a.K / kChunk;
-  const uint16_t* rows[8];
+  const uint16_t* rows[R];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) rows[r] = wrow(a, n0 + r) + 8 * lane;
+  for (int r = 0; r < R; ++r) rows[r] = wrow(a, n0 + r) + 8 * lane;
+  // the epilogue pair of this thread (threads t < KV / 2 of wave 0): its rotation is computed
+  // while the first loads are in flight
+  const int eb = t / (R / 2), en = n0 + 2 * (t % (R / 2));
+  const bool epi = t < KV / 2 && eb < a.B;
+  float2 cs = make_float2(1.f, 0.f);
 
-  float acc[NB][8];
+  float acc[NB][R];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[b][r] = 0.f;
+    for (int r = 0; r < R; ++r) acc[b][r] = 0.f;
 
   for (int c0 = wave; c0 < nch; c0 += 4 * U) {
-    u32x4 wv[U][8];
+    u32x4 wv[U][R];
     uint32_t xv[U][NB][XV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = min(c0 + 4 * u, nch - 1);   // past the end: reload the last chunk, unused
+      const int c = c0 + 4 * u;
+      if (c >= nch) break;                      // wave-uniform
 #pragma unroll
-      for (int r = 0; r < 8; ++r) wv[u][r] = *(const u32x4*)(rows[r] + (int64_t)c * kChunk);
+      for (int r = 0; r < R; ++r) wv[u][r] = *(const u32x4*)(rows[r] + (int64_t)c * kChunk);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int bb = min(b, a.B - 1);
@@ -132,13 +149,14 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
         }
       }
     }
+    if (c0 == wave && epi && en >= a.n_split) cs = rope_cs(a, eb, en);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + 4 * u < nch) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
+          for (int r = 0; r < R; ++r) {
             float s = acc[b][r];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -154,13 +172,11 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
   }
 
   // sum over the 64 lanes: each halving step halves the values a lane holds
-  constexpr int KV = NB * 8;
-  constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : NB == 4 ? 5 : 6;   // log2 KV
   float v[KV];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[b * 8 + r] = acc[b][r];
+    for (int r = 0; r < R; ++r) v[b * R + r] = acc[b][r];
 #pragma unroll
   for (int step = 0; step < LK; ++step) {
     const int d = 32 >> step;
@@ -173,53 +189,101 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
       v[i] = keep + __shfl_xor(send, d, 64);
     }
   }
+  // after LK steps lane l holds value (l >> (6 - LK)) summed over the lanes sharing that index
+  // bit pattern; finish over the remaining low lane bits
   float s = v[0];
 #pragma unroll
   for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
   const int idx = (lane >> (6 - LK)) & (KV - 1);
   if ((lane & ((64 >> LK) - 1)) == 0) red[wave][idx] = s;
   __syncthreads();
-  if (t < NB * 4) {
-    const int b = t >> 2, p = t & 3;
-    if (b < a.B) {
-      const int i0 = b * 8 + 2 * p;
-      const float v0 = ((red[0][i0] + red[1][i0]) + red[2][i0]) + red[3][i0];
-      const float v1 = ((red[0][i0 + 1] + red[1][i0 + 1]) + red[2][i0 + 1]) + red[3][i0 + 1];
-      store_pair<YBF16>(a, b, n0 + 2 * p, v0, v1);
-    }
+  if (epi) {
+    const int i0 = eb * R + (en - n0);
+    const float v0 = ((red[0][i0] + red[1][i0]) + red[2][i0]) + red[3][i0];
+    const float v1 = ((red[0][i0 + 1] + red[1][i0 + 1]) + red[2][i0 + 1]) + red[3][i0 + 1];
+    store_pair<YBF16>(a, eb, en, v0, v1, cs);
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// MFMA, B > 8.  grid (N / 32, ceil(B / 32), chunks), 64 threads.  Chunk z covers K elements
-// [z kc, (z + 1) kc), kc = K / chunks (a multiple of 256).
+// MFMA, B > 8.  grid (ceil(N / 128), ceil(B / 128), chunks), 256 threads.  The workgroup owns rows
+// [128 x, 128 x + 128) (wave w: 32 of them) and tokens [128 y, 128 y + 32 NT) over chunk z of K
+// (kc elements).  Per 64-element step of K the tokens' x (rounded to bf16) goes through LDS once
+// for all four waves (double buffered, one barrier per step), while each wave loads its rows'
+// W for the next step straight into registers in the MFMA operand layout (lane: row lane % 32,
+// 8 elements at 16 s + 8 (lane / 32)).  A = x (tokens), B = W (rows), D[token][row] in fp32.
 // ------------------------------------------------------------------------------------------------
-template <bool XF32>
-__global__ __launch_bounds__(64) void k_proj_mfma(ProjArgs a, int kc, float* __restrict__ part) {
-  const int lane = threadIdx.x;
-  const int jb = blockIdx.x, tb = blockIdx.y, z = blockIdx.z;
-  const int j = jb * 32 + (lane & 31);                    // W row (B operand column)
-  const int tok = min(tb * 32 + (lane & 31), a.B - 1);   // token (A operand row); rows past B repeat
-  const int k0 = z * kc + 8 * (lane >> 5);
-  const uint16_t* w = wrow(a, j) + k0;
-  f32x16 acc = {};
-  for (int ks = 0; ks < kc; ks += 256) {
-    u32x4 xa[16], wb[16];
+template <int NT, bool XF32>
+__global__ __launch_bounds__(256) void k_proj_mfma(ProjArgs a, int kc, float* __restrict__ part) {
+  constexpr int kStep = 64, kRowB = kStep * 2 + 16;       // LDS row: 64 bf16 + 16 bytes of skew
+  constexpr int TB = 32 * NT;
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][TB * kRowB];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row0 = blockIdx.x * kProjRows + 32 * wave;
+  const int tok0 = blockIdx.y * kProjToks;
+  const int kbeg = blockIdx.z * kc;
+  const bool active = row0 < a.N;                         // wave-uniform (N is a multiple of 32)
+  const uint16_t* w = wrow(a, active ? row0 + (lane & 31) : 0) + kbeg + 8 * (lane >> 5);
+
+  // x staging: TB tokens x 64 elements = TB * 8 pieces of 8 elements; thread t takes pieces t + 256 i
+  constexpr int XP = TB * 8 / 256;                        // = NT
+  u32x4 xr[XP];
+  auto load_x = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      xa[s] = load_x_bf16<XF32>(a, tok, k0 + ks + 16 * s);
-      wb[s] = *(const u32x4*)(w + ks + 16 * s);
+    for (int i = 0; i < XP; ++i) {
+      const int piece = t + 256 * i;
+      const int tok = min(tok0 + (piece >> 3), a.B - 1);  // tokens past B repeat the last (discarded)
+      xr[i] = load_x_bf16<XF32>(a, tok, k + 8 * (piece & 7));
     }
+  };
+  auto store_x = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = mfma32x32x16(xa[s], wb[s], acc);
-  }
-  // D layout: lane holds row j for tokens 8 (i / 4) + 4 (lane / 32) + i % 4
-  float* dst = part + (int64_t)z * a.B * a.N + j;
+    for (int i = 0; i < XP; ++i) {
+      const int piece = t + 256 * i;
+      *(u32x4*)&xs[buf][(piece >> 3) * kRowB + 16 * (piece & 7)] = xr[i];
+    }
+  };
+  u32x4 wr[2][4];
+  auto load_w = [&](int k, u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tt = tb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (tt < a.B) dst[(int64_t)tt * a.N] = acc[i];
+    for (int s = 0; s < 4; ++s) dst[s] = active ? *(const u32x4*)(w + (k - kbeg) + 16 * s) : u32x4{0, 0, 0, 0};
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x16{};
+  const int nsteps = kc / kStep;
+  load_x(kbeg);
+  load_w(kbeg, wr[0]);
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    store_x(buf);
+    __syncthreads();
+    if (st + 1 < nsteps) {
+      load_x(kbeg + (st + 1) * kStep);
+      load_w(kbeg + (st + 1) * kStep, wr[buf ^ 1]);
+    }
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const u32x4 xa = *(const u32x4*)&xs[buf][(32 * i + (lane & 31)) * kRowB + 32 * s + 16 * (lane >> 5)];
+          acc[i] = mfma32x32x16(xa, wr[buf][s], acc[i]);
+        }
+      }
+    }
   }
+  if (!active) return;
+  // D layout: lane holds row row0 + lane % 32 for tokens 8 (e / 4) + 4 (lane / 32) + e % 4
+  float* dst = part + (int64_t)blockIdx.z * a.B * a.N + row0 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tt = tok0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (tt < a.B) dst[(int64_t)tt * a.N] = acc[i][e];
+    }
 }
 
 // grid (ceil(N / 512), B), 256 threads: thread t owns outputs 2t, 2t + 1 of its 512-row block
@@ -242,7 +306,7 @@ __global__ __launch_bounds__(256) void k_proj_reduce(ProjArgs a, int nz, const f
         v1 += u[i].y;
       }
   }
-  store_pair<YBF16>(a, b, n, v0, v1);
+  store_pair<YBF16>(a, b, n, v0, v1, n >= a.n_split ? rope_cs(a, b, n) : make_float2(1.f, 0.f));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -294,25 +358,49 @@ __global__ __launch_bounds__(256) void k_fold(FoldArgs f) {
 // launchers
 // ------------------------------------------------------------------------------------------------
 namespace {
+template <int NB, bool XF32, bool YBF16>
+void launch_gemv_t(const ProjArgs& a, hipStream_t s) {
+  // rows per workgroup R and chunks in flight per wave U, from a sweep at the V3 shapes: one token
+  // streams best with few rows and a deep queue; from two tokens on the register budget (and so
+  // the waves per SIMD) decides, and more rows share each x load
+#ifdef PROJ_GEMV_R
+  constexpr int R = PROJ_GEMV_R;
+#else
+  constexpr int R = NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? 4 : NB == 4 ? (XF32 ? 4 : 2) : 8;
+#endif
+#ifdef PROJ_GEMV_U
+  constexpr int U = PROJ_GEMV_U;
+#else
+  constexpr int U = NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? (XF32 ? 2 : 1) : 1;
+#endif
+  hipLaunchKernelGGL((k_proj_gemv<NB, R, U, XF32, YBF16>), dim3(a.N / R), dim3(256), 0, s, a);
+}
+
 template <bool XF32, bool YBF16>
 hipError_t launch_gemv_nb(const ProjArgs& a, hipStream_t s) {
-  const dim3 grid(a.N / 8), block(256);
   if (a.B <= 1)
-    hipLaunchKernelGGL((k_proj_gemv<1, XF32, YBF16>), grid, block, 0, s, a);
+    launch_gemv_t<1, XF32, YBF16>(a, s);
   else if (a.B <= 2)
-    hipLaunchKernelGGL((k_proj_gemv<2, XF32, YBF16>), grid, block, 0, s, a);
+    launch_gemv_t<2, XF32, YBF16>(a, s);
   else if (a.B <= 4)
-    hipLaunchKernelGGL((k_proj_gemv<4, XF32, YBF16>), grid, block, 0, s, a);
+    launch_gemv_t<4, XF32, YBF16>(a, s);
   else
-    hipLaunchKernelGGL((k_proj_gemv<8, XF32, YBF16>), grid, block, 0, s, a);
+    launch_gemv_t<8, XF32, YBF16>(a, s);
   return hipGetLastError();
 }
 
 template <bool XF32, bool YBF16>
 hipError_t launch_proj_t(const ProjArgs& a, float* ws, hipStream_t s) {
   if (a.B <= kProjGemvMaxB) return launch_gemv_nb<XF32, YBF16>(a, s);
-  const int nz = proj_chunks(a.K);
-  hipLaunchKernelGGL((k_proj_mfma<XF32>), dim3(a.N / 32, (a.B + 31) / 32, nz), dim3(64), 0, s, a, a.K / nz, ws);
+  const int nz = proj_chunks(a.B, a.N, a.K);
+  const dim3 grid((a.N + kProjRows - 1) / kProjRows, (a.B + kProjToks - 1) / kProjToks, nz);
+  const int toks = a.B < kProjToks ? a.B : kProjToks;     // tokens of the widest workgroup
+  if (toks <= 32)
+    hipLaunchKernelGGL((k_proj_mfma<1, XF32>), grid, dim3(256), 0, s, a, a.K / nz, ws);
+  else if (toks <= 64)
+    hipLaunchKernelGGL((k_proj_mfma<2, XF32>), grid, dim3(256), 0, s, a, a.K / nz, ws);
+  else
+    hipLaunchKernelGGL((k_proj_mfma<4, XF32>), grid, dim3(256), 0, s, a, a.K / nz, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_proj_reduce<YBF16>), dim3((a.N + 511) / 512, a.B), dim3(256), 0, s, a, nz,

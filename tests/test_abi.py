@@ -236,10 +236,12 @@ def test_mha_decode_validation(lib):
 def test_projection_workspace_rules(lib):
     ws = lib.mla_proj_workspace_bytes
     assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0                # GEMV: none
-    # MFMA path: K split into chunks of a multiple of 256 elements, at most 2048, dividing K
-    assert ws(9, 1536, 7168) == 4 * 9 * 1536 * 4                              # 7168 = 4 x 1792
-    assert ws(64, 24576, 1536) == 1 * 64 * 24576 * 4
-    assert ws(128, 7168, 16384) == 8 * 128 * 7168 * 4
+    # MFMA path: tiles of 128 rows x 128 tokens; K split into d chunks, d the smallest divisor of
+    # K / 256 that gives at least 512 workgroups (else K / 256)
+    assert ws(9, 1536, 7168) == 28 * 9 * 1536 * 4                             # 12 tiles: 28 chunks
+    assert ws(64, 24576, 1536) == 3 * 64 * 24576 * 4                          # 192 tiles: 3 chunks
+    assert ws(128, 7168, 16384) == 16 * 128 * 7168 * 4                        # 56 tiles: 16 chunks
+    assert ws(129, 7168, 16384) == 8 * 129 * 7168 * 4                         # 112 tiles: 8 chunks
     assert ws(0, 32, 512) == 0
     q = lib.mla_query_workspace_bytes
     assert q(1, 7168, 1536, 128, 128, 64) == 0

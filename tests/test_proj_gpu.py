@@ -9,9 +9,9 @@ Bars (the kernels accumulate in fp32):
     of the exact c_q, relative L2 <= 3e-3, and with the exact c_q, <= 1e-2;
   * fp32 results of the GEMV path (up to 8 tokens, fp32 x): relative L2 <= 2e-5; of the MFMA path
     (x rounded to bf16 for the MFMA): <= 4e-3.
-Sizes: the V3 shapes (D 7168, d_q 1536, H 128, d_h 128, d_c 512, d_R 64) at 1, 3, 8 (largest GEMV),
-9 (first MFMA), 33 and 100 tokens (ragged 32-token tiles), a small non-V3 shape, positions 0 and
-32767, and B = 0.
+Sizes: the V3 shapes (D 7168, d_q 1536, H 128, d_h 128, d_c 512, d_R 64) at 1, 2, 3, 4, 8 (each
+GEMV variant), 9, 33, 100 (the MFMA tile widths, ragged 32-token blocks) and 130 tokens (two
+128-token tiles), a small non-V3 shape, positions 0 and 32767, and B = 0.
 """
 from __future__ import annotations
 
@@ -52,7 +52,7 @@ def _say(msg):
 # ------------------------------------------------------------------------------------ query side
 @pytest.fixture(scope="module")
 def v3_query():
-    big = make_query_inputs(100)
+    big = make_query_inputs(130)
     W = {k: decode_bf16(getattr(big, k)) for k in ("W_DQ", "W_UQ", "W_QR")}
     dev = {k: _bf16_tensor(getattr(big, k)) for k in ("W_DQ", "W_UQ", "W_QR", "W_UK")}
     return big, W, dev
@@ -75,7 +75,7 @@ def _check_query(inp, W, dev, B, H, rope_base=10000.0):
     assert relative_l2(got_C, ex_C) <= 1e-2 and relative_l2(got_R, ex_R) <= 1e-2
 
 
-@pytest.mark.parametrize("B", [1, 3, 8, 9, 33, 100])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 9, 33, 100, 130])
 def test_query_proj_v3(v3_query, B):
     inp, W, dev = v3_query
     _say(f"mla_query_proj V3 B={B}")
@@ -171,11 +171,11 @@ def test_folded_query_matches_unfolded_oracle(v3_query):
 # ------------------------------------------------------------------------------------ output side
 @pytest.fixture(scope="module")
 def v3_output():
-    inp = make_output_inputs(40)
+    inp = make_output_inputs(130)
     return inp, decode_bf16(inp.W_O), _bf16_tensor(inp.W_O), _bf16_tensor(inp.W_UV)
 
 
-@pytest.mark.parametrize("B", [1, 2, 5, 8, 9, 40])
+@pytest.mark.parametrize("B", [1, 2, 5, 8, 9, 40, 100, 130])
 def test_out_proj_v3(v3_output, B):
     inp, W_O, dW_O, _ = v3_output
     _say(f"mla_out_proj V3 B={B}")
