@@ -154,3 +154,11 @@ def test_config_shapes():
     assert (w[2].B, w[2].H, w[2].d_c, w[2].d_R, w[2].n_max) == (1, 128, 512, 64, 4096)
     assert w[3].layout == "packed" and w[4].layout == "paged" and w[5].dtype == "fp8"
     assert math.isclose(w[2].scale, 1 / math.sqrt(192)) and math.isclose(w[1].scale, 1 / math.sqrt(24))
+
+
+def test_smoke_inputs_build_on_the_host():
+    # the inputs of __graft_entry__.smoke() are built without a GPU
+    import __graft_entry__ as g
+    cases = g.smoke_inputs()
+    assert len(cases) == 2
+    assert list(cases[1][0].lens) == [96, 33, 1]
