@@ -20,7 +20,7 @@
 //    [chunk][token][576] float32.
 //  * k_append_finalize: one workgroup per token adds the chunks in order, rotates the rope pairs
 //    (angles in double precision), encodes, and stores the row.
-#include "mla_internal.h"
+#include "rows_internal.h"
 
 namespace mla {
 

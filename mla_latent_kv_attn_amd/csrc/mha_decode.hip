@@ -17,7 +17,7 @@
 // online softmax (maximum, sum, 32-value accumulator per lane) in log2 units; at the end the
 // lanes of a wave and then the four waves are merged, and the split's (m, l, acc[128]) is written.
 // k_mha_combine: grid (H, B), 128 threads: the log-sum-exp merge of the W splits.
-#include "mla_internal.h"
+#include "rows_internal.h"
 
 namespace mla {
 

@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-#include "mla_internal.h"
+#include "rows_internal.h"
 
 namespace {
 

@@ -59,17 +59,6 @@ struct CombineArgs {
   float* lse;                   // [B, H] or nullptr
 };
 
-// cache write: destination rows (element strides as in mla_cache_desc)
-struct AppendArgs {
-  void* latent;
-  void* rope;
-  float* latent_scale;
-  const int32_t* block_table;
-  int64_t lat_sb, lat_st, rope_sb, rope_st, scale_sb;
-  int page_size, max_pages;
-  float rope_base;
-};
-
 // workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, then the
 // counters and per-quarter outputs of the fused combine + uv pass, each 256-byte aligned.  A slot
 // of the acc block holds H x d_c floats, row-major [slot][H][d_c]: the partial pass writes whole
@@ -98,49 +87,6 @@ inline size_t ws_prefix_off(int W, int B, int H, int d_c) { return ws_ml_off(W, 
 inline size_t ws_cnt_off(int W, int B, int H, int d_c) { return ws_prefix_off(W, B, H, d_c) + ws_prefix_bytes(B); }
 inline size_t ws_uv_off(int W, int B, int H, int d_c) { return ws_cnt_off(W, B, H, d_c) + ws_cnt_bytes(H); }
 
-// projections y[b, n] = sum_k W[n, k] x[b, k] (proj.hip).  Rows n < n_split come from w0 and are
-// scaled and stored to y; rows n >= n_split come from w1 (row n - n_split) and are the rotary rows,
-// turned per 64-row head block at pos[b] and stored to y1 as bf16.  N % 32 == 0, K % 512 == 0.
-constexpr int kProjGemvMaxB = 8;   // up to this many tokens: the GEMV kernel (no workspace)
-struct ProjArgs {
-  const uint16_t* w0;
-  const uint16_t* w1;
-  int n_split;
-  int64_t ldw;                  // row stride of w0 and w1 (elements)
-  const void* x;                // [B, K] bf16 or fp32, row stride ldx
-  int64_t ldx;
-  int B, N, K;
-  float scale;                  // applied to rows below n_split
-  void* y;                      // [B, n_split] (row stride ldy), bf16 or fp32
-  int64_t ldy;
-  void* y1;                     // [B, N - n_split] bf16 (row stride ldy1), the rotated rows
-  int64_t ldy1;
-  const int32_t* pos;           // [B] positions of the rotary rows
-  float rope_base;
-};
-// MFMA path (B > kProjGemvMaxB): workgroup tiles of 128 rows x up to 128 tokens; K is split into
-// proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups
-constexpr int kProjRows = 128, kProjToks = 128;
-inline int proj_chunks(int B, int N, int K) {
-  const int64_t blocks = (int64_t)((N + kProjRows - 1) / kProjRows) * ((B + kProjToks - 1) / kProjToks);
-  const int units = K / 256;
-  for (int d = 1; d <= units; ++d)
-    if (units % d == 0 && blocks * d >= 512) return d;
-  return units;
-}
-size_t proj_ws_bytes(int B, int N, int K);
-
-// per-head weight fold C_h[m, n] = sum_{i < inner} A_h[m, i] B_h[i, n] (bf16 in, fp32 sums, bf16 out)
-struct FoldArgs {
-  const uint16_t* A;
-  int64_t a_sh, a_sm, a_si;
-  const uint16_t* B;
-  int64_t b_sh, b_si;           // column stride 1
-  uint16_t* C;
-  int64_t c_sh, c_sm;           // column stride 1
-  int H, M, Nc, inner;          // M % 64 == 0, Nc % 64 == 0, inner % 32 == 0
-};
-
 // launchers (return the launch error; host-side validation happens in mla_abi.cpp)
 hipError_t launch_absorb_f32(const float* q, const float* w, float* out, int B, int H, int d_h, int d_c,
                              hipStream_t s);
@@ -155,14 +101,6 @@ hipError_t launch_uv_bf16w_generic(const float* o_lat, const void* w, float* out
                                    int d_c, hipStream_t s);
 hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, int H, hipStream_t s);
 hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s);
-size_t append_ws_bytes(int B, int D);
-size_t mha_ws_bytes(int B, int H, int W);
-hipError_t launch_mha(const void* q, const void* kc, const void* vc, const int32_t* lens, int B, int H, int64_t cap,
-                      float scale, int W, float* ws, float* out, float* lse, hipStream_t s);
-hipError_t launch_proj(const ProjArgs& a, bool x_f32, bool y_bf16, float* ws, hipStream_t s);
-hipError_t launch_fold(const FoldArgs& f, hipStream_t s);
-hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
-                         const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s);
 
 }  // namespace mla
 

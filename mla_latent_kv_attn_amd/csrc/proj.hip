@@ -30,7 +30,7 @@
 // k_fold: the per-head product of two weight matrices with fp32 accumulation and a bf16 result,
 // C_h = A_h B_h (A_h [M, 128] and B_h [128, Nc], both through strides), used offline for
 // W_QK_h = W_UK_h^T W_UQ_h and W_OV_h = W_O[:, h] W_UV_h.
-#include "mla_internal.h"
+#include "rows_internal.h"
 
 namespace mla {
 
