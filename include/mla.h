@@ -319,8 +319,8 @@ size_t mla_query_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R)
  *   workspace at least mla_query_workspace_bytes(...) bytes (NULL allowed when that is 0),
  *         16-byte aligned, any contents; overwritten
  * c_q is rounded to bf16 before the second projection reads it.  No normalisation is applied.
- * Supported: dtype MLA_BF16, d_R == 64, d_h even, D and d_q multiples of 512, d_q and
- * H (d_h + d_R) multiples of 32, 16-byte aligned pointers.  B == 0 is a no-op.  Two projections
+ * Supported: dtype MLA_BF16, d_R == 64, d_h even, H d_h a multiple of 8, D and d_q multiples of
+ * 512, d_q and H (d_h + d_R) multiples of 32, B D < 2^31, 16-byte aligned pointers.  B == 0 is a no-op.  Two projections
  * on `stream` (one kernel each up to 8 tokens, two beyond).
  */
 int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, int dtype,
@@ -339,8 +339,8 @@ int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void
  * from q_C, computed from c_q with the folded weights.
  *   c_q [B, d_q] bf16, W_QK [H, d_c, d_q] bf16, q_abs [B, H, d_c] written, MLA_BF16 or MLA_F32
  *   workspace at least mla_proj_workspace_bytes(B, H d_c, d_q) bytes (NULL allowed when 0)
- * Supported: dtype MLA_BF16, d_q a multiple of 512, H d_c a multiple of 32, 16-byte aligned
- * pointers.  B == 0 is a no-op.
+ * Supported: dtype MLA_BF16, d_q a multiple of 512, H d_c a multiple of 32, B d_q < 2^31,
+ * 16-byte aligned pointers.  B == 0 is a no-op.
  */
 int mla_fold_q(const void* W_UQ, const void* W_UK, int dtype, void* W_QK, int H, int d_h, int d_c, int d_q,
                void* stream);
@@ -354,8 +354,8 @@ int mla_absorb_q_folded(const void* c_q, const void* W_QK, int dtype, void* q_ab
  *       the latent outputs [B, H, d_c] of mla_decode_attn (K = H d_c, W = W_OV from mla_fold_o)
  *   W   [D, K] bf16, out [B, D] float32 written
  *   workspace at least mla_proj_workspace_bytes(B, D, K) bytes (NULL allowed when 0)
- * Supported: w_dtype MLA_BF16, D a multiple of 32, K a multiple of 512, 16-byte aligned
- * pointers.  B == 0 is a no-op.
+ * Supported: w_dtype MLA_BF16, D a multiple of 32, K a multiple of 512, B K < 2^30, 16-byte
+ * aligned pointers.  B == 0 is a no-op.
  *
  * mla_fold_o -- W_UV merged into W_O once when the weights are loaded ("Grouped-query and latent
  * attention", section "The absorption trick"):

@@ -419,6 +419,8 @@ int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int 
 // ------------------------------------------------------------------------------------------------
 namespace {
 bool proj_shape_ok(int N, int K) { return N >= 32 && (N % 32) == 0 && K >= 512 && (K % 512) == 0; }
+// the MFMA projection addresses x with 32-bit byte offsets
+bool proj_x_fits(int B, int K, int elem_bytes) { return (int64_t)B * K * elem_bytes < ((int64_t)1 << 32); }
 
 mla::ProjArgs proj_args(const void* w0, const void* w1, int n_split, const void* x, int B, int N, int K) {
   mla::ProjArgs a{};
@@ -460,7 +462,8 @@ int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void
   if (!h || !W_DQ || !W_UQ || !W_QR || !pos || !c_q || !q_C || !q_R) return MLA_ERR_NULL;
   if (dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   const int64_t n2 = (int64_t)H * (d_h + d_R);
-  if (d_R != 64 || (d_h % 2) != 0 || !proj_shape_ok(d_q, D) || n2 > (1 << 30) || !proj_shape_ok((int)n2, d_q))
+  if (d_R != 64 || (d_h % 2) != 0 || ((H * d_h) % 8) != 0 || !proj_shape_ok(d_q, D) || n2 > (1 << 30) ||
+      !proj_shape_ok((int)n2, d_q) || !proj_x_fits(B, D, 2))
     return MLA_ERR_UNSUPPORTED;
   if (!aligned16(h) || !aligned16(W_DQ) || !aligned16(W_UQ) || !aligned16(W_QR) || !aligned16(c_q) ||
       !aligned16(q_C) || !aligned16(q_R))
@@ -494,7 +497,7 @@ int mla_absorb_q_folded(const void* c_q, const void* W_QK, int dtype, void* q_ab
   if (!c_q || !W_QK || !q_abs) return MLA_ERR_NULL;
   if (dtype != MLA_BF16 || !(out_dtype == MLA_BF16 || out_dtype == MLA_F32)) return MLA_ERR_UNSUPPORTED;
   const int64_t n = (int64_t)H * d_c;
-  if (n > (1 << 30) || !proj_shape_ok((int)n, d_q)) return MLA_ERR_UNSUPPORTED;
+  if (n > (1 << 30) || !proj_shape_ok((int)n, d_q) || !proj_x_fits(B, d_q, 2)) return MLA_ERR_UNSUPPORTED;
   if (!aligned16(c_q) || !aligned16(W_QK) || !aligned16(q_abs)) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::proj_ws_bytes(B, (int)n, d_q);
   if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
@@ -511,7 +514,7 @@ int mla_out_proj(const float* x, const void* W, int w_dtype, float* out, int B, 
   if (!known_dtype(w_dtype)) return MLA_ERR_DTYPE;
   if (B == 0) return MLA_OK;
   if (!x || !W || !out) return MLA_ERR_NULL;
-  if (w_dtype != MLA_BF16 || !proj_shape_ok(D, K)) return MLA_ERR_UNSUPPORTED;
+  if (w_dtype != MLA_BF16 || !proj_shape_ok(D, K) || !proj_x_fits(B, K, 4)) return MLA_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(W) || !aligned16(out)) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::proj_ws_bytes(B, D, K);
   if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;

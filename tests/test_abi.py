@@ -266,6 +266,7 @@ def test_query_proj_validation(lib):
     assert call(D=7000) == L.MLA_ERR_UNSUPPORTED
     assert call(d_q=1000) == L.MLA_ERR_UNSUPPORTED
     assert call(h=FAKE + 2) == L.MLA_ERR_UNSUPPORTED
+    assert call(H=3, d_h=6) == L.MLA_ERR_UNSUPPORTED                      # q_C rows not a multiple of 8
     need = lib.mla_query_workspace_bytes(64, 7168, 1536, 128, 128, 64)
     assert call(B=64) == L.MLA_ERR_WORKSPACE
     assert call(B=64, wsp=FAKE, wsb=need - 1) == L.MLA_ERR_WORKSPACE
@@ -291,3 +292,4 @@ def test_fold_and_out_proj_validation(lib):
     assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 1, 7168, 16000, None, 0, None) == L.MLA_ERR_UNSUPPORTED
     assert op(FAKE + 4, FAKE, L.MLA_BF16, FAKE, 1, 7168, 16384, None, 0, None) == L.MLA_ERR_UNSUPPORTED
     assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 9, 7168, 16384, None, 0, None) == L.MLA_ERR_WORKSPACE
+    assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 16384, 7168, 65536, FAKE, 1 << 40, None) == L.MLA_ERR_UNSUPPORTED
