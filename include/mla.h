@@ -292,13 +292,13 @@ int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int 
 /*
  * Projections around the attention core.  Each is y[b, n] = sum_k W[n, k] x[b, k] over a bf16
  * weight W [N, K] (row n maps x to output n, the column-vector form y = W x) with fp32
- * accumulation.  Up to 8 tokens: a streaming GEMV, no workspace needed.  More tokens: bf16 MFMA
- * (fp32 x is rounded to bf16 for it) split over K, partial sums in the workspace, added in a
- * fixed order.  Deterministic.
+ * accumulation.  1-2 tokens, or up to 8 tokens when K >= 4096: a streaming GEMV, no workspace
+ * needed.  Otherwise: bf16 MFMA (fp32 x is rounded to bf16 for it) split over K, partial sums in
+ * the workspace, added in a fixed order.  Deterministic.
  *
  * mla_proj_workspace_bytes: workspace of one projection with B tokens, N outputs, K inputs
- * (0 when B <= 8); mla_query_workspace_bytes: workspace of mla_query_proj (the larger of its two
- * projections).  0 for invalid sizes.
+ * (0 when the GEMV serves it); mla_query_workspace_bytes: workspace of mla_query_proj (the larger
+ * of its two projections).  0 for invalid sizes.
  */
 size_t mla_proj_workspace_bytes(int B, int N, int K);
 size_t mla_query_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R);
@@ -321,7 +321,7 @@ size_t mla_query_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R)
  * c_q is rounded to bf16 before the second projection reads it.  No normalisation is applied.
  * Supported: dtype MLA_BF16, d_R == 64, d_h even, H d_h a multiple of 8, D and d_q multiples of
  * 512, d_q and H (d_h + d_R) multiples of 32, B D < 2^31, 16-byte aligned pointers.  B == 0 is a no-op.  Two projections
- * on `stream` (one kernel each up to 8 tokens, two beyond).
+ * on `stream` (one kernel each on the GEMV path, two on the MFMA path).
  */
 int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, int dtype,
                    const int32_t* pos, int B, int D, int d_q, int H, int d_h, int d_R, float rope_base, void* c_q,

@@ -9,14 +9,15 @@
 //    section "The absorption trick").
 //
 // For the few tokens of a decode step every weight byte is used B times, so the work is a
-// stream of the weights from HBM.  Two kernels:
-//  * k_proj_gemv (B <= 8): one workgroup (4 waves) per R rows of W (R = 2, 4 or 8 by batch) over
+// stream of the weights from HBM.  Two kernels (the GEMV for 1-2 tokens, and for up to 8 when K
+// >= 4096; the MFMA path otherwise):
+//  * k_proj_gemv: one workgroup (4 waves) per R rows of W (R = 2, 4 or 8 by batch) over
 //    the whole of K.  K is cut into 512-element chunks; wave w takes chunks w, w + 4, ... with U
 //    chunks' loads in flight together.  Lane l reads elements 8l .. 8l+7 of a chunk of each of the
 //    R rows (every load instruction is one contiguous KiB of a row) and of each token's x, keeps
 //    R x NB fp32 product sums, and the sums are reduced over the 64 lanes (halving exchange) and
 //    then over the 4 waves through LDS.  No workspace.
-//  * k_proj_mfma (B > 8): bf16 MFMA 32x32x16 with fp32 accumulation on tiles of 128 rows x up
+//  * k_proj_mfma: bf16 MFMA 32x32x16 with fp32 accumulation on tiles of 128 rows x up
 //    to 128 tokens (4 waves of 32 rows), split over K in chunks (grid z) so that the weights
 //    stream from many CUs at once; x (fp32 rounded to bf16) is staged once per workgroup through
 //    LDS, W comes straight from global memory in the MFMA operand layout (16 contiguous bytes of
@@ -89,7 +90,7 @@ __device__ __forceinline__ u32x4 load_x_bf16(const ProjArgs& a, int b, int k) {
 }  // namespace
 
 size_t proj_ws_bytes(int B, int N, int K) {
-  if (B <= kProjGemvMaxB) return 0;
+  if (proj_uses_gemv(B, K)) return 0;
   return (size_t)proj_chunks(B, N, K) * (size_t)B * (size_t)N * sizeof(float);
 }
 
@@ -391,7 +392,7 @@ hipError_t launch_gemv_nb(const ProjArgs& a, hipStream_t s) {
 
 template <bool XF32, bool YBF16>
 hipError_t launch_proj_t(const ProjArgs& a, float* ws, hipStream_t s) {
-  if (a.B <= kProjGemvMaxB) return launch_gemv_nb<XF32, YBF16>(a, s);
+  if (proj_uses_gemv(a.B, a.K)) return launch_gemv_nb<XF32, YBF16>(a, s);
   const int nz = proj_chunks(a.B, a.N, a.K);
   const dim3 grid((a.N + kProjRows - 1) / kProjRows, (a.B + kProjToks - 1) / kProjToks, nz);
   const int toks = a.B < kProjToks ? a.B : kProjToks;     // tokens of the widest workgroup

@@ -20,7 +20,10 @@ struct AppendArgs {
 // projections y[b, n] = sum_k W[n, k] x[b, k] (proj.hip).  Rows n < n_split come from w0 and are
 // scaled and stored to y; rows n >= n_split come from w1 (row n - n_split) and are the rotary rows,
 // turned per 64-row head block at pos[b] and stored to y1 as bf16.  N % 32 == 0, K % 512 == 0.
-constexpr int kProjGemvMaxB = 8;   // up to this many tokens: the GEMV kernel (no workspace)
+constexpr int kProjGemvMaxB = 8;   // the GEMV kernel serves at most this many tokens
+// GEMV (no workspace) for 1-2 tokens, and for up to 8 when K is long (>= 4096); otherwise the
+// MFMA path (whose 32-token tile costs about the same from 1 to 32 tokens) is faster
+inline bool proj_uses_gemv(int B, int K) { return B <= 2 || (B <= kProjGemvMaxB && K >= 4096); }
 struct ProjArgs {
   const uint16_t* w0;
   const uint16_t* w1;
@@ -37,7 +40,7 @@ struct ProjArgs {
   const int32_t* pos;           // [B] positions of the rotary rows
   float rope_base;
 };
-// MFMA path (B > kProjGemvMaxB): workgroup tiles of 128 rows x up to 128 tokens; K is split into
+// MFMA path (otherwise): workgroup tiles of 128 rows x up to 128 tokens; K is split into
 // proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups
 constexpr int kProjRows = 128, kProjToks = 128;
 inline int proj_chunks(int B, int N, int K) {

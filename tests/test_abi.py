@@ -235,7 +235,9 @@ def test_mha_decode_validation(lib):
 
 def test_projection_workspace_rules(lib):
     ws = lib.mla_proj_workspace_bytes
-    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0                # GEMV: none
+    # GEMV (no workspace): 1-2 tokens, or up to 8 with K >= 4096
+    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0 and ws(2, 24576, 1536) == 0
+    assert ws(3, 24576, 1536) == 3 * 3 * 24576 * 4                            # K < 4096: MFMA path
     # MFMA path: tiles of 128 rows x 128 tokens; K split into d chunks, d the smallest divisor of
     # K / 256 that gives at least 512 workgroups (else K / 256)
     assert ws(9, 1536, 7168) == 28 * 9 * 1536 * 4                             # 12 tiles: 28 chunks
@@ -244,7 +246,8 @@ def test_projection_workspace_rules(lib):
     assert ws(129, 7168, 16384) == 8 * 129 * 7168 * 4                         # 112 tiles: 8 chunks
     assert ws(0, 32, 512) == 0
     q = lib.mla_query_workspace_bytes
-    assert q(1, 7168, 1536, 128, 128, 64) == 0
+    assert q(1, 7168, 1536, 128, 128, 64) == 0 and q(2, 7168, 1536, 128, 128, 64) == 0
+    assert q(8, 7168, 1536, 128, 128, 64) == ws(8, 128 * 192, 1536) > 0     # second pass on MFMA
     assert q(64, 7168, 1536, 128, 128, 64) == max(ws(64, 1536, 7168), ws(64, 128 * 192, 1536))
 
 

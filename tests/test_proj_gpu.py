@@ -7,11 +7,12 @@ Bars (the kernels accumulate in fp32):
     value, or (where a fold's fp32 sum of 128 products may cancel) relative L2 <= 2.5e-3;
   * q_C / q_R read c_q rounded to bf16: compared with the oracle applied to its own bf16 rounding
     of the exact c_q, relative L2 <= 3e-3, and with the exact c_q, <= 1e-2;
-  * fp32 results of the GEMV path (up to 8 tokens, fp32 x): relative L2 <= 2e-5; of the MFMA path
-    (x rounded to bf16 for the MFMA): <= 4e-3.
-Sizes: the V3 shapes (D 7168, d_q 1536, H 128, d_h 128, d_c 512, d_R 64) at 1, 2, 3, 4, 8 (each
-GEMV variant), 9, 33, 100 (the MFMA tile widths, ragged 32-token blocks) and 130 tokens (two
-128-token tiles), a small non-V3 shape, positions 0 and 32767, and B = 0.
+  * fp32 results of the GEMV path (fp32 x): relative L2 <= 2e-5; of the MFMA path (x rounded to
+    bf16 for the MFMA): <= 4e-3.
+Sizes: the V3 shapes (D 7168, d_q 1536, H 128, d_h 128, d_c 512, d_R 64) at 1, 2, 3, 4, 8 (the GEMV
+variants, and the MFMA path from 3 tokens where K < 4096), 9, 33, 100 (the MFMA tile widths,
+ragged 32-token blocks) and 130 tokens (two 128-token tiles), a small non-V3 shape, positions 0
+and 32767, and B = 0.
 """
 from __future__ import annotations
 
