@@ -488,7 +488,7 @@ def main_proj(args):
                                "(timed here as the whole mla_query_proj); its own weight read is W_QK",
                                "weight_bytes_unfolded": w_main + H * d_h * d_c * 2,
                                "weight_bytes_folded": nbytes([base["W_DQ"], base["W_QR"], W_QK])},
-            "roofline": {"bound": "hbm", "kernel": "mla_query_proj (%s)" % ("k_proj_gemv x2" if B <= 2 else
+            "roofline": {"bound": "hbm", "kernel": "mla_query_proj (%s)" % ("k_proj_gemv x2" if B <= 4 else
                                                                            "k_proj_gemv, k_proj_mfma + k_proj_reduce"
                                                                            if B <= 8 else
                                                                            "k_proj_mfma + k_proj_reduce, x2"),

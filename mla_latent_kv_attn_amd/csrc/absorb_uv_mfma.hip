@@ -7,7 +7,7 @@
 // ("Grouped-query and latent attention", section "The absorption trick".)  The MFMA kernels read
 // the weight once per 128 (absorb) / 32 (uv) batch rows; for B <= 4 the streaming kernels below
 // read it once, as plain bandwidth-bound passes over the 16.8 MB weight.
-#include "mla_internal.h"
+#include "lane_reduce.h"
 
 namespace mla {
 
@@ -173,14 +173,12 @@ __global__ __launch_bounds__(256) void k_uv_bf16(const float* __restrict__ o_lat
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b0 = bz * 32;
   // stage: thread t converts 8 consecutive columns (8 (t % 64) ..) of rows t / 64 + 4 j
-  for (int r = tid >> 6; r < 32; r += 4) {
-    const int b = b0 + r;
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (b < B) {
-      const float* src = o_lat + ((int64_t)b * H + h) * 512 + 8 * lane;
-      x0 = *(const float4*)src;
-      x1 = *(const float4*)(src + 4);
-    }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (tid >> 6) + 4 * j;
+    // rows past B read the last token (all loads in flight together; their outputs are not stored)
+    const float* src = o_lat + ((int64_t)min(b0 + r, B - 1) * H + h) * 512 + 8 * lane;
+    const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
     u32x4 hi, lo;
     split_hi_lo(x0, x1, hi, lo);
     *(u32x4*)(xs[0] + r * kUvRow + 16 * lane) = hi;
@@ -230,12 +228,9 @@ __global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat
   float x[NB][8];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (b < B) {
-      const float* xp = o_lat + ((int64_t)b * H + h) * 512 + 8 * lane;
-      x0 = *(const float4*)xp;
-      x1 = *(const float4*)(xp + 4);
-    }
+    // tokens past B read the last one (all loads in flight together; their outputs are not stored)
+    const float* xp = o_lat + ((int64_t)min(b, B - 1) * H + h) * 512 + 8 * lane;
+    const float4 x0 = *(const float4*)xp, x1 = *(const float4*)(xp + 4);
     x[b][0] = x0.x; x[b][1] = x0.y; x[b][2] = x0.z; x[b][3] = x0.w;
     x[b][4] = x1.x; x[b][5] = x1.y; x[b][6] = x1.z; x[b][7] = x1.w;
   }
@@ -253,21 +248,7 @@ __global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat
       v[b * 8 + r] = s;
     }
   // halving exchange over lane bits 5, 4, ...: afterwards lane l holds value (l >> (6 - LK)) & (K - 1)
-#pragma unroll
-  for (int step = 0; step < LK; ++step) {
-    const int d = 32 >> step;
-    const int half = K >> (step + 1);
-    const bool upper = (lane & d) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, d, 64);
-    }
-  }
-  float t = v[0];
-#pragma unroll
-  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+  const float t = lane_sum_halving<K>(v, lane);
   const int idx = (lane >> (6 - LK)) & (K - 1);
   const int b = idx >> 3, r = idx & 7;
   if ((lane & ((64 >> LK) - 1)) == 0 && b < B) out[((int64_t)b * H + h) * 128 + i0 + r] = t;

@@ -20,6 +20,7 @@
 //    [chunk][token][576] float32.
 //  * k_append_finalize: one workgroup per token adds the chunks in order, rotates the rope pairs
 //    (angles in double precision), encodes, and stores the row.
+#include "lane_reduce.h"
 #include "rows_internal.h"
 
 namespace mla {
@@ -100,23 +101,8 @@ __global__ __launch_bounds__(64) void k_append_gemv(const uint16_t* __restrict__
       v[b * 8 + r] = acc;
     }
   constexpr int LK = NB == 1 ? 3 : NB == 2 ? 4 : NB == 4 ? 5 : 6;   // log2 K
-#pragma unroll
-  for (int step = 0; step < LK; ++step) {
-    const int d = 32 >> step;
-    const int half = K >> (step + 1);
-    const bool upper = (lane & d) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, d, 64);
-    }
-  }
-  // after LK steps lane l holds the partial of value index (l >> (6 - LK)) summed over the lanes
-  // that share it; finish over the remaining 64 / K lane bits
-  float t = v[0];
-#pragma unroll
-  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+  // lane l ends with the full sum of value index (l >> (6 - LK))
+  const float t = lane_sum_halving<K>(v, lane);
   const int idx = (lane >> (6 - LK)) & (K - 1);
   const int b = idx >> 3, r = idx & 7;
   if ((lane & ((64 >> LK) - 1)) == 0 && b < B) part[((int64_t)ks * B + b) * kOut + 8 * g + r] = t;

@@ -9,8 +9,8 @@
 //    section "The absorption trick").
 //
 // For the few tokens of a decode step every weight byte is used B times, so the work is a
-// stream of the weights from HBM.  Two kernels (the GEMV for 1-2 tokens, and for up to 8 when K
-// >= 4096; the MFMA path otherwise):
+// stream of the weights from HBM.  Two kernels (the GEMV for up to 4 tokens, and for up to 8 when
+// K >= 4096; the MFMA path otherwise):
 //  * k_proj_gemv: one workgroup (4 waves) per R rows of W (R = 2, 4 or 8 by batch) over
 //    the whole of K.  K is cut into 512-element chunks; wave w takes chunks w, w + 4, ... with U
 //    chunks' loads in flight together.  Lane l reads elements 8l .. 8l+7 of a chunk of each of the
@@ -31,6 +31,7 @@
 // k_fold: the per-head product of two weight matrices with fp32 accumulation and a bf16 result,
 // C_h = A_h B_h (A_h [M, 128] and B_h [128, Nc], both through strides), used offline for
 // W_QK_h = W_UK_h^T W_UQ_h and W_OV_h = W_O[:, h] W_UV_h.
+#include "lane_reduce.h"
 #include "rows_internal.h"
 
 namespace mla {
@@ -178,23 +179,8 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < R; ++r) v[b * R + r] = acc[b][r];
-#pragma unroll
-  for (int step = 0; step < LK; ++step) {
-    const int d = 32 >> step;
-    const int half = KV >> (step + 1);
-    const bool upper = (lane & d) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, d, 64);
-    }
-  }
-  // after LK steps lane l holds value (l >> (6 - LK)) summed over the lanes sharing that index
-  // bit pattern; finish over the remaining low lane bits
-  float s = v[0];
-#pragma unroll
-  for (int d = (32 >> (LK - 1)) >> 1; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  // lane l ends with the full sum of value index (l >> (6 - LK))
+  const float s = lane_sum_halving<KV>(v, lane);
   const int idx = (lane >> (6 - LK)) & (KV - 1);
   if ((lane & ((64 >> LK) - 1)) == 0) red[wave][idx] = s;
   __syncthreads();
@@ -367,7 +353,7 @@ void launch_gemv_t(const ProjArgs& a, hipStream_t s) {
 #ifdef PROJ_GEMV_R
   constexpr int R = PROJ_GEMV_R;
 #else
-  constexpr int R = NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? 4 : NB == 4 ? (XF32 ? 4 : 2) : 8;
+  constexpr int R = NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? 4 : NB == 4 ? (XF32 ? 8 : 4) : (XF32 ? 8 : 2);
 #endif
 #ifdef PROJ_GEMV_U
   constexpr int U = PROJ_GEMV_U;

@@ -21,9 +21,9 @@ struct AppendArgs {
 // scaled and stored to y; rows n >= n_split come from w1 (row n - n_split) and are the rotary rows,
 // turned per 64-row head block at pos[b] and stored to y1 as bf16.  N % 32 == 0, K % 512 == 0.
 constexpr int kProjGemvMaxB = 8;   // the GEMV kernel serves at most this many tokens
-// GEMV (no workspace) for 1-2 tokens, and for up to 8 when K is long (>= 4096); otherwise the
+// GEMV (no workspace) for up to 4 tokens, and for up to 8 when K is long (>= 4096); otherwise the
 // MFMA path (whose 32-token tile costs about the same from 1 to 32 tokens) is faster
-inline bool proj_uses_gemv(int B, int K) { return B <= 2 || (B <= kProjGemvMaxB && K >= 4096); }
+inline bool proj_uses_gemv(int B, int K) { return B <= 4 || (B <= kProjGemvMaxB && K >= 4096); }
 struct ProjArgs {
   const uint16_t* w0;
   const uint16_t* w1;

@@ -235,9 +235,9 @@ def test_mha_decode_validation(lib):
 
 def test_projection_workspace_rules(lib):
     ws = lib.mla_proj_workspace_bytes
-    # GEMV (no workspace): 1-2 tokens, or up to 8 with K >= 4096
-    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0 and ws(2, 24576, 1536) == 0
-    assert ws(3, 24576, 1536) == 3 * 3 * 24576 * 4                            # K < 4096: MFMA path
+    # GEMV (no workspace): up to 4 tokens, or up to 8 with K >= 4096
+    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0 and ws(4, 24576, 1536) == 0
+    assert ws(5, 24576, 1536) == 3 * 5 * 24576 * 4                            # K < 4096: MFMA path
     # MFMA path: tiles of 128 rows x 128 tokens; K split into d chunks, d the smallest divisor of
     # K / 256 that gives at least 512 workgroups (else K / 256)
     assert ws(9, 1536, 7168) == 28 * 9 * 1536 * 4                             # 12 tiles: 28 chunks
