@@ -301,11 +301,13 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
     const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml[s H]
     const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 128 * q + 4 * c4;   // + s H 512
     const float2 q0 = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
+    // segments past nseg read the last one (weight 0 below): all loads go out together, where a
+    // conditional load would be waited on before the next one is issued
     float4 x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int su = sg + 8 * u;
-      x[u] = su < nseg ? *(const float4*)(src + su * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int su = min(sg + 8 * u, max(nseg - 1, 0));
+      x[u] = *(const float4*)(src + su * sstride);
     }
     if (b == 0) {
       const uint16_t* wp = w + ((int64_t)h * 128 + (tid >> 1)) * 512 + 128 * q + 64 * (tid & 1);

@@ -203,27 +203,21 @@ __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
   if (col < d_c) {
     const float* acc0 = a.ws_acc + ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at acc0 + H d_c s
     const int64_t astride = (int64_t)H * d_c;
-    int s = sg;
-    for (; s + 24 < nseg; s += 32) {
+    // four segments per pass, all four loads in flight together; in the last pass segments past
+    // nseg read the last one and get weight 0 (a load per remaining segment would be waited on
+    // one by one)
+    for (int s = sg; s < nseg; s += 32) {
       float4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(acc0 + (s + 8 * u) * astride);
+      for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(acc0 + min(s + 8 * u, nseg - 1) * astride);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float f = weight(s + 8 * u);
+        const float f = s + 8 * u < nseg ? weight(s + 8 * u) : 0.f;
         o.x = fmaf(f, v[u].x, o.x);
         o.y = fmaf(f, v[u].y, o.y);
         o.z = fmaf(f, v[u].z, o.z);
         o.w = fmaf(f, v[u].w, o.w);
       }
-    }
-    for (; s < nseg; s += 8) {
-      const float4 v = *(const float4*)(acc0 + s * astride);
-      const float f = weight(s);
-      o.x = fmaf(f, v.x, o.x);
-      o.y = fmaf(f, v.y, o.y);
-      o.z = fmaf(f, v.z, o.z);
-      o.w = fmaf(f, v.w, o.w);
     }
   }
   red[sg][c4] = o;
