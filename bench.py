@@ -71,11 +71,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--row", choices=["decode", "append", "mha", "query", "out"], default="decode",
+    ap.add_argument("--row", choices=["decode", "append", "mha", "query", "out", "layer"], default="decode",
                     help="decode: the absorbed decode step (default); append: the cache write of one step; "
                          "mha: the same-dimension MHA decode beside the latent path's attention pass; "
                          "query: the query side (c_q, q_C, q_R, then q' unfolded or through the folded "
-                         "W_UK^T W_UQ); out: the output side (W_UV then W_O, or the folded W_O W_UV)")
+                         "W_UK^T W_UQ); out: the output side (W_UV then W_O, or the folded W_O W_UV); "
+                         "layer: one whole attention layer's decode step (cache write, query side, "
+                         "attention, W_UV, W_O)")
+    ap.add_argument("--layer-context", type=int, default=4096,
+                    help="--row layer: tokens per sequence after the new one is appended")
     ap.add_argument("--append-batch", type=int, default=1,
                     help="--row append / query / out: new tokens (sequences) per call")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
@@ -185,6 +189,9 @@ def main():
         return
     if args.row in ("query", "out"):
         main_proj(args)
+        return
+    if args.row == "layer":
+        main_layer(args)
         return
 
     from mla_latent_kv_attn_amd import ops
@@ -559,6 +566,97 @@ def main_proj(args):
             dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(n * B / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"{n} oracle passes over the same {B} tokens (float64 numpy), {dt:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def main_layer(args):
+    """One whole attention layer's decode step (DecodeLayer) at the V3 shape: B sequences of
+    --layer-context tokens after the new token is appended; bf16 weights (373 MB per layer) and
+    caches rotated over enough copies to miss the 256 MB Infinity Cache, the calls in a HIP graph."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_attn_amd import ops
+    from mla_latent_kv_attn_amd.layer import DecodeLayer
+    from workloads.layer import make_layer_inputs
+
+    B, N = args.append_batch, args.layer_context
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    inp = make_layer_inputs([N - 1] * B, N)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base_w = {k: bf16(v) for k, v in inp.weights.items()}
+    w_bytes = sum(t.numel() * 2 for t in base_w.values())
+    cache_bytes = B * N * (512 + 64) * 2
+    R = max(1, min(16, math.ceil(args.rotate_mb * 1e6 / (w_bytes + cache_bytes))))
+    layers = []
+    for r in range(R):
+        w = base_w if r == 0 else {k: v.clone() for k, v in base_w.items()}
+        cache = ops.Cache.split(bf16(inp.latent), bf16(inp.rope))
+        layers.append(DecodeLayer(w, cache, B, max_len=N))
+    h = bf16(inp.h)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    seq_lens = torch.from_numpy(inp.pos + 1).to(dev)
+    us, calls = _graph_time_us([lambda L=L: L(h, pos, seq_lens, stream=stream) for L in layers], args.steps, stream)
+    alg = w_bytes + cache_bytes + B * 7168 * 2 + B * 7168 * 4
+    achieved = alg / (us * 1e-6) / 1e9
+    out = {
+        "metric": "attention-layer decode steps/sec x tokens (V3 shape, whole layer)",
+        "value": round(B / (us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": calls, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
+        "config": {"workload": f"V3 attention layer decode, B={B} sequences x {N} tokens: cache write, query side, "
+                               "absorbed attention, W_UV, W_O", "B": B, "context": N, "graph": True,
+                   "copies_rotated": R},
+        "roofline": {"bound": "hbm", "kernel": "whole layer (11-14 kernels)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "alg_bytes_per_launch": alg, "avg_us": round(us, 3)},
+    }
+    if args.cpu_seconds > 0:
+        import threadpoolctl
+        import oracle
+        import oracle.output as oo
+        import oracle.query as oq
+        from oracle import decode_bf16
+        from oracle.cache_write import cache_row, encode_bf16
+        from workloads.configs import Workload
+        from workloads.gen import DecodeInputs
+        cores = len(os.sched_getaffinity(0))
+        W = {k: decode_bf16(v) for k, v in inp.weights.items()}
+        hh = decode_bf16(inp.h)
+
+        def held(x):
+            return decode_bf16(encode_bf16(x))
+
+        def once():
+            row = cache_row(hh, W["W_DKV"], W["W_KR"], inp.pos)
+            q_C, q_R = oq.q_up(W["W_UQ"], W["W_QR"], held(oq.q_down(W["W_DQ"], hh)), inp.pos, 128)
+            lat = decode_bf16(inp.latent).astype(np.float32)
+            rp = decode_bf16(inp.rope).astype(np.float32)
+            lat[:, N - 1] = decode_bf16(row["c_bf16"])
+            rp[:, N - 1] = decode_bf16(row["k_R_bf16"])
+            wl = Workload("layer", seed=0, B=B, H=128, d_h=128, d_c=512, d_R=64, n_max=N, len_lo=N, len_hi=N,
+                          dtype="f32", layout="split")
+            d = DecodeInputs(wl=wl, lens=np.full(B, N, np.int32), q_C=held(q_C).astype(np.float32),
+                             q_R=held(q_R).astype(np.float32), W_UK=W["W_UK"].astype(np.float32),
+                             W_UV=W["W_UV"].astype(np.float32), latent=lat, rope=rp)
+            oo.out_proj(W["W_O"], oracle.decode(d, want_diag=False)["o"])
+
+        with threadpoolctl.threadpool_limits(limits=cores):
+            info = threadpoolctl.threadpool_info()
+            threads = max([i.get("num_threads", 1) for i in info] or [1])
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds:
+                once()
+                n += 1
+            dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n * B / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{n} oracle layer passes over the same {B} tokens (float64 numpy), {dt:.1f} s"}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
