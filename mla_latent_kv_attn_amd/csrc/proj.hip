@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_fold(FoldArgs f) {
 // launchers
 // ------------------------------------------------------------------------------------------------
 namespace {
-template <int NB, bool XF32, bool YBF16>
+template <int NB, bool XF32, bool YBF16, int RK = 0>
 void launch_gemv_t(const ProjArgs& a, hipStream_t s) {
   // rows per workgroup R and chunks in flight per wave U, from a sweep at the V3 shapes: one token
   // streams best with few rows and a deep queue; from two tokens on the register budget (and so
@@ -353,7 +353,7 @@ void launch_gemv_t(const ProjArgs& a, hipStream_t s) {
 #ifdef PROJ_GEMV_R
   constexpr int R = PROJ_GEMV_R;
 #else
-  constexpr int R = NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? 4 : NB == 4 ? (XF32 ? 8 : 4) : (XF32 ? 8 : 2);
+  constexpr int R = RK ? RK : NB == 1 ? (XF32 ? 4 : 2) : NB == 2 ? 4 : NB == 4 ? (XF32 ? 8 : 4) : (XF32 ? 8 : 2);
 #endif
 #ifdef PROJ_GEMV_U
   constexpr int U = PROJ_GEMV_U;
@@ -365,8 +365,13 @@ void launch_gemv_t(const ProjArgs& a, hipStream_t s) {
 
 template <bool XF32, bool YBF16>
 hipError_t launch_gemv_nb(const ProjArgs& a, hipStream_t s) {
-  if (a.B <= 1)
-    launch_gemv_t<1, XF32, YBF16>(a, s);
+  if (a.B <= 1) {
+    // one token, bf16 x: short rows (K < 4096, 3 KiB) stream better with 4 rows per workgroup
+    if (!XF32 && a.K < 4096)
+      launch_gemv_t<1, XF32, YBF16, 4>(a, s);
+    else
+      launch_gemv_t<1, XF32, YBF16>(a, s);
+  }
   else if (a.B <= 2)
     launch_gemv_t<2, XF32, YBF16>(a, s);
   else if (a.B <= 4)

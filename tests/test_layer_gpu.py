@@ -85,3 +85,37 @@ def test_decode_layer_matches_oracle(lens):
             step = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
             assert np.all(np.abs(g - exact) <= step * 1.0001 + 1e-6)
         assert np.array_equal(lat_h[b, :p], inp.latent[b, :p]) and np.array_equal(lat_h[b, p + 1:], inp.latent[b, p + 1:])
+
+
+def test_decode_layer_graph_replays_match_eager():
+    # the whole layer captured once in a HIP graph; several replays with eager work and
+    # synchronisations between them, each checked against the eager result (bitwise: same kernels,
+    # same launch shapes, deterministic reductions)
+    print("DecodeLayer graph replays", flush=True)
+    lens = [17, 200, 64]
+    cap = 256
+    inp = make_layer_inputs(lens, cap, seed=53)
+    B = len(lens)
+    weights = {k: _dev(v) for k, v in inp.weights.items()}
+    lat, rope = _dev(inp.latent), _dev(inp.rope)
+    cache = ops.Cache.split(lat, rope)
+    pos = torch.from_numpy(inp.pos).cuda()
+    seq_lens = torch.from_numpy(inp.pos + 1).cuda()
+    h = _dev(inp.h)
+    layer = DecodeLayer(weights, cache, B, max_len=cap)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager = layer(h, pos, seq_lens, stream=stream).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        layer(h, pos, seq_lens, stream=stream)
+    for rep in range(3):
+        layer.y.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()      # eager work between replays
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, eager), f"replay {rep} differs from the eager layer"
+        assert torch.isfinite(junk)
