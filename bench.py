@@ -398,8 +398,9 @@ def main_append(args):
         "dtype": "bf16", "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
         "config": {"workload": f"V3 cache write, B={B} new tokens, hidden 7168 -> latent 512 + rope 64, bf16 split cache",
                    "B": B, "D": D, "graph": True, "input_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "mla_cache_append (%s + k_append_finalize)"
-                                                % ("k_append_gemv" if B <= 8 else "k_append_proj"),
+        "roofline": {"bound": "hbm", "kernel": "mla_cache_append (%s)"
+                                                % ("k_proj_gemv, writing the cache row" if B <= 8 else
+                                                   "k_append_proj + k_append_finalize"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "alg_bytes_per_launch": alg,
                      "avg_us": round(us, 3)},

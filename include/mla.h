@@ -255,8 +255,10 @@ size_t mla_cache_append_workspace_bytes(int B, int D);
  * rounded to nearest even; an MLA_FP8_E4M3 latent stores OCP E4M3 codes RNE(clamp(c/s, +-448))
  * with the float32 scale s = amax/448 over the row (s = 1 when the row is zero) in latent_scale.
  * Supported: d_c == 512, d_R == 64, D a multiple of 512, rope MLA_BF16, latent MLA_BF16 or
- * MLA_FP8_E4M3, contiguous or paged, 16-byte aligned pointers and rows, B <= 65535.  B == 0 is a
- * no-op.  Two kernel launches on `stream`; deterministic.
+ * MLA_FP8_E4M3, contiguous or paged, 16-byte aligned pointers and rows, B <= 65535, B D < 2^31.
+ * B == 0 is a no-op.  Deterministic.  Up to 8 tokens a bf16 cache row is written by the
+ * projection itself (one kernel); otherwise, and for E4M3 (which needs the row's amax first), the
+ * projection's chunk partials are finished by a second kernel.
  */
 int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dtype, const int32_t* pos,
                      const mla_cache_desc* cache, int B, int D, int d_c, int d_R, float rope_base, void* workspace,

@@ -9,7 +9,11 @@
 // scale amax/448 (RNE of the clamped c/s), into the contiguous or paged layouts the decode path
 // reads.
 //
-// Two passes:
+// bf16 caches, up to 8 tokens: one projection y = [W_DKV; W_KR] h through the projection GEMV
+// (proj.hip), whose epilogue writes the row (and rotates the rope pairs) straight into the cache.
+// E4M3 caches need the amax of the whole latent row before any code is chosen, and beyond 8
+// tokens the 576 outputs are too few rows to spread a one-pass projection over the chip, so
+// those take two passes:
 //  * k_append_gemv (B <= 8): a streaming GEMV over coalesced weight rows, split over D in chunks
 //    of 512 (see below);
 //  * k_append_proj (B > 8): the projection [B x D] . [D x 576] on bf16 MFMA 32x32x16 with fp32
@@ -31,6 +35,7 @@ constexpr int kKChunk = 512;       // D elements per projection chunk
 }  // namespace
 
 size_t append_ws_bytes(int B, int D) {
+  // chunk partials of the two-pass form (the one-pass form needs none)
   return (size_t)(D / kKChunk) * (size_t)B * kOut * sizeof(float);
 }
 
@@ -182,23 +187,41 @@ __global__ __launch_bounds__(256) void k_append_finalize(const float* __restrict
   }
   if (!FP8) {
     *(uint32_t*)((uint16_t*)a.latent + lrow + 2 * t) = pack_bf16x2(lat.x, lat.y);
-  } else {
-    float m = fmaxf(fabsf(lat.x), fabsf(lat.y));
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    const float y0 = fminf(fmaxf(lat.x / s, -448.0f), 448.0f);
-    const float y1 = fminf(fmaxf(lat.y / s, -448.0f), 448.0f);
-    *(uint16_t*)((uint8_t*)a.latent + lrow + 2 * t) = (uint16_t)(e4m3_code(y0) | (e4m3_code(y1) << 8));
-    if (t == 0) a.latent_scale[srow] = s;
+    return;
   }
+  float m = fmaxf(fabsf(lat.x), fabsf(lat.y));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float y0 = fminf(fmaxf(lat.x / s, -448.0f), 448.0f);
+  const float y1 = fminf(fmaxf(lat.y / s, -448.0f), 448.0f);
+  *(uint16_t*)((uint8_t*)a.latent + lrow + 2 * t) = (uint16_t)(e4m3_code(y0) | (e4m3_code(y1) << 8));
+  if (t == 0) a.latent_scale[srow] = s;
 }
 
 hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
                          const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s) {
+  if (!fp8 && B <= kProjGemvMaxB) {
+    ProjArgs pa{};
+    pa.w0 = (const uint16_t*)w_dkv;
+    pa.w1 = (const uint16_t*)w_kr;
+    pa.n_split = kOut - 64;
+    pa.ldw = D;
+    pa.x = h;
+    pa.ldx = D;
+    pa.B = B;
+    pa.N = kOut;
+    pa.K = D;
+    pa.scale = 1.f;
+    pa.pos = pos;
+    pa.rope_base = a.rope_base;
+    pa.dst_cache = 1;
+    pa.cache = a;
+    return launch_proj(pa, false, true, ws, s);
+  }
   if (B <= 8) {
     const dim3 g0(kOut / 8, D / kKChunk);
 #define MLA_GEMV(NB) hipLaunchKernelGGL(k_append_gemv<NB>, g0, dim3(64), 0, s, (const uint16_t*)h, \

@@ -338,7 +338,8 @@ int mla_cache_append(const void* h, const void* W_DKV, const void* W_KR, int dty
   if (dtype != MLA_BF16 || cache->rope_dtype != MLA_BF16 ||
       !(cache->latent_dtype == MLA_BF16 || cache->latent_dtype == MLA_FP8_E4M3))
     return MLA_ERR_UNSUPPORTED;
-  if (d_c != 512 || d_R != 64 || D < 512 || (D % 512) != 0 || B > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d_c != 512 || d_R != 64 || D < 512 || (D % 512) != 0 || B > 65535 || (int64_t)B * D * 2 >= ((int64_t)1 << 32))
+    return MLA_ERR_UNSUPPORTED;
   const bool fp8 = cache->latent_dtype == MLA_FP8_E4M3;
   const bool paged = cache->block_table != nullptr;
   if (fp8 && !cache->latent_scale) return MLA_ERR_NULL;

@@ -26,7 +26,10 @@
 // Both end in the same epilogue on pairs of adjacent outputs (n, n + 1), n even: rows below
 // n_split are scaled and stored to y (bf16 or fp32); rows from n_split on are the rotary rows
 // (pairs (2i, 2i+1) of each 64-row head block turned by pos[b] * base^(-2i/64), angle and its
-// sine and cosine in double precision) stored to y1 as bf16.
+// sine and cosine in double precision) stored to y1 as bf16.  For the cache write (bf16 caches)
+// both go straight into the new token's cache row at pos[b]: latent = W_DKV h, rope key =
+// RoPE_pos(W_KR h) ("MLA storage: Representing KV with a small latent vector", section "Storing a
+// positional key separately").
 //
 // k_fold: the per-head product of two weight matrices with fp32 accumulation and a bf16 result,
 // C_h = A_h B_h (A_h [M, 128] and B_h [128, Nc], both through strides), used offline for
@@ -56,6 +59,27 @@ __device__ __forceinline__ float2 rope_cs(const ProjArgs& a, int b, int n) {
 // the epilogue of one output pair (n, n + 1) of token b; cs is the pair's rotation when n >= n_split
 template <bool YBF16>
 __device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, float v0, float v1, float2 cs) {
+  if (a.dst_cache) {
+    // the cache write: token b's new row at pos[b] (contiguous, or through the block table)
+    const AppendArgs& c = a.cache;
+    const int ps = a.pos[b];
+    int64_t lrow, rrow;
+    if (c.block_table) {
+      const int page = c.block_table[(int64_t)b * c.max_pages + ps / c.page_size];
+      const int slot = ps % c.page_size;
+      lrow = (int64_t)page * c.lat_sb + (int64_t)slot * c.lat_st;
+      rrow = (int64_t)page * c.rope_sb + (int64_t)slot * c.rope_st;
+    } else {
+      lrow = (int64_t)b * c.lat_sb + (int64_t)ps * c.lat_st;
+      rrow = (int64_t)b * c.rope_sb + (int64_t)ps * c.rope_st;
+    }
+    if (n < a.n_split)
+      *(uint32_t*)((uint16_t*)c.latent + lrow + n) = pack_bf16x2(v0, v1);
+    else
+      *(uint32_t*)((uint16_t*)c.rope + rrow + (n - a.n_split)) =
+          pack_bf16x2(v0 * cs.x - v1 * cs.y, v0 * cs.y + v1 * cs.x);
+    return;
+  }
   if (n < a.n_split) {
     v0 *= a.scale;
     v1 *= a.scale;

@@ -39,6 +39,8 @@ struct ProjArgs {
   int64_t ldy1;
   const int32_t* pos;           // [B] positions of the rotary rows
   float rope_base;
+  int dst_cache;                // 1: rows < n_split go to the cache latent row of token b at pos[b],
+  AppendArgs cache;             //    the rotated rows to its rope row (bf16; y, y1 unused)
 };
 // MFMA path (otherwise): workgroup tiles of 128 rows x up to 128 tokens; K is split into
 // proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups

@@ -180,6 +180,7 @@ def test_partial_warm_validation(lib):
 def test_cache_append_validation(lib):
     f = lib.mla_cache_append
     ws = lib.mla_cache_append_workspace_bytes
+    # the two-pass form's 14 chunk partials (the one-pass bf16 form up to 8 tokens needs none)
     assert ws(1, 7168) == 14 * 1 * 576 * 4 and ws(128, 7168) == 14 * 128 * 576 * 4
     assert ws(0, 7168) == 0 and ws(1, 7000) == 0 and ws(1, 0) == 0
     good_ws = ws(4, 7168)
