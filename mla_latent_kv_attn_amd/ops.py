@@ -37,6 +37,17 @@ def _dev(*ts):
             raise ValueError("tensors must be on a HIP device")
 
 
+def _scratch(nbytes: int, like: torch.Tensor, stream=None) -> torch.Tensor:
+    """A workspace the wrapper allocates itself.  torch frees it when the wrapper returns, while the
+    kernels may still be running: on the current stream torch reuses the memory only in stream
+    order; on another stream the tensor is recorded on that stream first, so that torch waits for
+    its work before reusing the memory."""
+    w = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    if stream is not None:
+        w.record_stream(stream)
+    return w
+
+
 def _stream(stream, t: torch.Tensor) -> int:
     s = stream if stream is not None else torch.cuda.current_stream(t.device)
     return int(s.cuda_stream)
@@ -134,7 +145,7 @@ def mla_decode_attn(q_abs: torch.Tensor, q_R: torch.Tensor, cache: Cache, seq_le
         raise ValueError("q_abs and q_R must be contiguous")
     need = mla_decode_workspace_bytes(B, H, d_c, max_len, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_abs.device)
+        workspace = _scratch(need, q_abs, stream)
     if o_latent is None:
         o_latent = torch.empty((B, H, d_c), dtype=torch.float32, device=q_abs.device)
     if lse is None and want_lse:
@@ -240,7 +251,7 @@ def mla_cache_append(h: torch.Tensor, W_DKV: torch.Tensor, W_KR: torch.Tensor, p
     if pos.dtype != torch.int32:
         raise TypeError("pos is int32")
     if workspace is None:
-        workspace = torch.empty(max(mla_cache_append_workspace_bytes(B, D), 1), dtype=torch.uint8, device=h.device)
+        workspace = _scratch(mla_cache_append_workspace_bytes(B, D), h, stream)
     check("mla_cache_append", _lib.lib().mla_cache_append(
         h.data_ptr(), W_DKV.data_ptr(), W_KR.data_ptr(), dtype_code(h), pos.data_ptr(), ctypes.byref(cache.desc), B,
         D, d_c, d_R, float(rope_base), workspace.data_ptr(), workspace.numel(), _stream(stream, h)))
@@ -260,19 +271,14 @@ def _contig(**ts):
             raise ValueError(f"{name} must be contiguous")
 
 
-def _ws(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
-    """(address, size) of the workspace: the caller's, else a fresh one of nbytes (none when 0).
-    A fresh one stays referenced until the next call on the device allocates another."""
+def _ws(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor], stream=None):
+    """(address, size) of the workspace: the caller's, else a fresh one of nbytes (none when 0)."""
     if workspace is not None:
         return workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if nbytes == 0:
         return 0, 0
-    w = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
-    _WS_HOLD[like.device] = w
+    w = _scratch(nbytes, like, stream)
     return w.data_ptr(), nbytes
-
-
-_WS_HOLD = {}
 
 
 def mla_query_proj(h: torch.Tensor, W_DQ: torch.Tensor, W_UQ: torch.Tensor, W_QR: torch.Tensor, pos: torch.Tensor,
@@ -295,7 +301,7 @@ def mla_query_proj(h: torch.Tensor, W_DQ: torch.Tensor, W_UQ: torch.Tensor, W_QR
         q_C = torch.empty(B, H, d_h, dtype=torch.bfloat16, device=h.device)
     if q_R is None:
         q_R = torch.empty(B, H, d_R, dtype=torch.bfloat16, device=h.device)
-    wp, wn = _ws(mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R), h, workspace)
+    wp, wn = _ws(mla_query_workspace_bytes(B, D, d_q, H, d_h, d_R), h, workspace, stream)
     check("mla_query_proj", _lib.lib().mla_query_proj(
         h.data_ptr(), W_DQ.data_ptr(), W_UQ.data_ptr(), W_QR.data_ptr(), dtype_code(h), pos.data_ptr(), B, D, d_q,
         H, d_h, d_R, float(rope_base), c_q.data_ptr(), q_C.data_ptr(), q_R.data_ptr(), wp, wn, _stream(stream, h)))
@@ -324,7 +330,7 @@ def mla_absorb_q_folded(c_q: torch.Tensor, W_QK: torch.Tensor, out: Optional[tor
     H, d_c = W_QK.shape[0], W_QK.shape[1]
     if out is None:
         out = torch.empty(B, H, d_c, dtype=out_dtype, device=c_q.device)
-    wp, wn = _ws(mla_proj_workspace_bytes(B, H * d_c, d_q), c_q, workspace)
+    wp, wn = _ws(mla_proj_workspace_bytes(B, H * d_c, d_q), c_q, workspace, stream)
     check("mla_absorb_q_folded", _lib.lib().mla_absorb_q_folded(
         c_q.data_ptr(), W_QK.data_ptr(), dtype_code(c_q), out.data_ptr(), dtype_code(out), B, H, d_c, d_q, wp, wn,
         _stream(stream, c_q)))
@@ -345,7 +351,7 @@ def mla_out_proj(x: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] =
         raise ValueError(f"W has {W.shape[1]} columns, x has {K} values per token")
     if out is None:
         out = torch.empty(B, D, dtype=torch.float32, device=x.device)
-    wp, wn = _ws(mla_proj_workspace_bytes(B, D, K), x, workspace)
+    wp, wn = _ws(mla_proj_workspace_bytes(B, D, K), x, workspace, stream)
     check("mla_out_proj", _lib.lib().mla_out_proj(x.data_ptr(), W.data_ptr(), dtype_code(W), out.data_ptr(), B, D,
                                                   K, wp, wn, _stream(stream, x)))
     return out
@@ -384,8 +390,7 @@ def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if out is None:
         out = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(max(mla_mha_decode_workspace_bytes(B, H, max_len, num_splits), 1), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _scratch(mla_mha_decode_workspace_bytes(B, H, max_len, num_splits), q, stream)
     check("mla_mha_decode", _lib.lib().mla_mha_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), dtype_code(q), seq_lens.data_ptr(), int(max_len), cap,
         B, H, d_k, d_v, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(), out.data_ptr(),
