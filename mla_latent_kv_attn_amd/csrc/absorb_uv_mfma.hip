@@ -19,30 +19,37 @@ namespace mla {
 // ---------------------------------------------------------------------------------------------
 constexpr int kAbsStride = 256 + 16;  // LDS row stride (bf16 elements): 544 B = 8 dwords mod 64 banks
 
-__global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
+// (q is not __restrict__: an invariant load could be sunk below the LDS stores and the barrier,
+// which costs a second memory round trip)
+__global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const uint16_t* __restrict__ w,
                                                      uint16_t* __restrict__ out, int B, int H) {
   __shared__ __attribute__((aligned(16))) uint16_t Ws[128 * kAbsStride];
   const int h = blockIdx.x, half = blockIdx.y, bz = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // all 16 loads of the thread's share of the slice go out before the first LDS store (one memory
+  // round trip, not one per group), and so do the q rows (rows past B read the last one; their
+  // outputs are not stored)
   const uint16_t* wsrc = w + (int64_t)h * 128 * 512 + half * 256;
-#pragma unroll 4
-  for (int c = tid; c < 128 * 32; c += 256) {
-    const int row = c >> 5, ch = c & 31;
-    const u32x4 v = *(const u32x4*)(wsrc + row * 512 + ch * 8);
-    *(u32x4*)(&Ws[row * kAbsStride + ch * 8]) = v;
-  }
-  __syncthreads();
-
   const int b0 = bz * 128 + wave * 32;
-  if (b0 >= B) return;
-  const int brow = b0 + (lane & 31), kh = lane >> 5;
+  const int brow = min(b0 + (lane & 31), B - 1), kh = lane >> 5;
   u32x4 aq[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (brow < B) aq[ks] = *(const u32x4*)(q + ((int64_t)brow * H + h) * 128 + 16 * ks + 8 * kh);
-    else aq[ks] = u32x4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < 8; ++ks) aq[ks] = *(const u32x4*)(q + ((int64_t)brow * H + h) * 128 + 16 * ks + 8 * kh);
+  u32x4 wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = tid + 256 * i, row = c >> 5, ch = c & 31;
+    wv[i] = *(const u32x4*)(wsrc + row * 512 + ch * 8);
   }
+  asm volatile("" ::: "memory");   // keeps every load above issued before the first store below
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = tid + 256 * i, row = c >> 5, ch = c & 31;
+    *(u32x4*)(&Ws[row * kAbsStride + ch * 8]) = wv[i];
+  }
+  __syncthreads();
+  if (b0 >= B) return;
   const int G = lane >> 4, r4 = (lane & 15) >> 2, q4 = lane & 3;
   uint16_t* orow = out + (int64_t)h * 512 + half * 256 + (lane & 31);
 #pragma unroll 1
@@ -172,32 +179,43 @@ __global__ __launch_bounds__(256) void k_uv_bf16(const float* __restrict__ o_lat
   const int h = blockIdx.x, bz = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b0 = bz * 32;
+  const int i0 = wave * 32;
+  const int kh = lane >> 5;
+  // this wave's 32 weight rows for all 32 k-steps, loaded before anything waits (one memory
+  // round trip for the whole workgroup, together with the o_lat rows below)
+  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh;
+  u32x4 bw[32];
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) bw[ks] = *(const u32x4*)(wr + 16 * ks);
   // stage: thread t converts 8 consecutive columns (8 (t % 64) ..) of rows t / 64 + 4 j
+  float4 xv[16];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (tid >> 6) + 4 * j;
-    // rows past B read the last token (all loads in flight together; their outputs are not stored)
+    // rows past B read the last token (their outputs are not stored)
     const float* src = o_lat + ((int64_t)min(b0 + r, B - 1) * H + h) * 512 + 8 * lane;
-    const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+    xv[2 * j] = *(const float4*)src;
+    xv[2 * j + 1] = *(const float4*)(src + 4);
+  }
+  asm volatile("" ::: "memory");   // keeps every load above issued before the first store below
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (tid >> 6) + 4 * j;
     u32x4 hi, lo;
-    split_hi_lo(x0, x1, hi, lo);
+    split_hi_lo(xv[2 * j], xv[2 * j + 1], hi, lo);
     *(u32x4*)(xs[0] + r * kUvRow + 16 * lane) = hi;
     *(u32x4*)(xs[1] + r * kUvRow + 16 * lane) = lo;
   }
   __syncthreads();
-  const int i0 = wave * 32;
-  const int kh = lane >> 5;
-  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh;
   const uint8_t* ahi = xs[0] + (lane & 31) * kUvRow + 16 * kh;
   const uint8_t* alo = xs[1] + (lane & 31) * kUvRow + 16 * kh;
   f32x16 acc = {}, acc2 = {};
-#pragma unroll 8
+#pragma unroll
   for (int ks = 0; ks < 32; ++ks) {
-    const u32x4 bw = *(const u32x4*)(wr + 16 * ks);
     const u32x4 hi = *(const u32x4*)(ahi + 32 * ks);
     const u32x4 lo = *(const u32x4*)(alo + 32 * ks);
-    acc = mfma32x32x16(hi, bw, acc);
-    acc2 = mfma32x32x16(lo, bw, acc2);
+    acc = mfma32x32x16(hi, bw[ks], acc);
+    acc2 = mfma32x32x16(lo, bw[ks], acc2);
   }
   float* orow = out + (int64_t)h * 128 + i0 + (lane & 31);
 #pragma unroll
