@@ -319,11 +319,13 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
     const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml[s H]
     const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 128 * q + 4 * c4;   // + s H 512
     const float2 q0 = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
-    // segments past nseg read the last one (weight 0 below): all loads go out together, where a
-    // conditional load would be waited on before the next one is issued
-    float4 x[4];
+    // the first 64 segments (8 per thread), all loads in flight together: segments past nseg read
+    // the last one (weight 0 below), where a conditional or looped load would be waited on before
+    // the next one is issued
+    constexpr int kPre = 8;
+    float4 x[kPre];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kPre; ++u) {
       const int su = min(sg + 8 * u, max(nseg - 1, 0));
       x[u] = *(const float4*)(src + su * sstride);
     }
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
     const float Ls = (rr[0] + rr[1]) + (rr[2] + rr[3]);
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kPre; ++u) {
       const int su = sg + 8 * u;
       const float f = su < nseg ? wts[su] : 0.f;
       o.x = fmaf(f, x[u].x, o.x);
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
       o.z = fmaf(f, x[u].z, o.z);
       o.w = fmaf(f, x[u].w, o.w);
     }
-    for (int s = sg + 32; s < nseg; s += 8) {
+    for (int s = sg + 8 * kPre; s < nseg; s += 8) {
       const float4 xs = *(const float4*)(src + s * sstride);
       const float f = s < kW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M);
       o.x = fmaf(f, xs.x, o.x);
