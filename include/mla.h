@@ -330,6 +330,23 @@ int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void
                    void* q_C, void* q_R, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_query_proj_append -- mla_query_proj and mla_cache_append of the same new tokens in two
+ * projections instead of three: W_DQ, W_DKV and W_KR all project h, so one pass over the stacked
+ * rows [W_DQ; W_DKV; W_KR] writes c_q and the new cache row (latent, and the rope key turned at
+ * pos) together; the second pass is mla_query_proj's.  Arguments as for those two calls; the
+ * cache must be bf16 (latent and rope; E4M3 caches need the row's amax first: use the two
+ * calls).  workspace: at least mla_query_append_workspace_bytes(B, D, d_q, H, d_h, d_R, d_c)
+ * bytes (NULL allowed when 0).  Up to 8 tokens the results are bitwise those of the two separate
+ * calls; beyond, c_q, q_C and q_R still are, and the cache row is the same sums in another order.
+ * Supported: dtype MLA_BF16, d_c == 512, d_R == 64, and mla_query_proj's shape rules.
+ */
+size_t mla_query_append_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R, int d_c);
+int mla_query_proj_append(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, const void* W_DKV,
+                          const void* W_KR, int dtype, const int32_t* pos, const mla_cache_desc* cache, int B, int D,
+                          int d_q, int H, int d_h, int d_R, int d_c, float rope_base, void* c_q, void* q_C, void* q_R,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_fold_q -- the absorbed query projection, folded once when the weights are loaded
  * ("The Journey to Multi-Head Latent Attention", section "The absorption trick (the magic)"):
  *   W_QK[h] = W_UK[h]^T W_UQ[h d_h : (h+1) d_h, :]      [H, d_c, d_q] bf16 written

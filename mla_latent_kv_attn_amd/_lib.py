@@ -83,6 +83,11 @@ _SIGS = {
     "mla_query_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "mla_query_proj": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 6
                        + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_query_append_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 7),
+    "mla_query_proj_append": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_void_p,
+                                                                      ctypes.POINTER(CacheDesc)]
+                              + [ctypes.c_int] * 7 + [ctypes.c_float] + [ctypes.c_void_p] * 4
+                              + [ctypes.c_size_t, ctypes.c_void_p]),
     "mla_fold_q": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
                    + [ctypes.c_int] * 4 + [ctypes.c_void_p]),
     "mla_absorb_q_folded": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]

@@ -207,7 +207,9 @@ hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, con
   if (!fp8 && B <= kProjGemvMaxB) {
     ProjArgs pa{};
     pa.w0 = (const uint16_t*)w_dkv;
+    pa.wc = (const uint16_t*)w_dkv;
     pa.w1 = (const uint16_t*)w_kr;
+    pa.n_cache = 0;
     pa.n_split = kOut - 64;
     pa.ldw = D;
     pa.x = h;

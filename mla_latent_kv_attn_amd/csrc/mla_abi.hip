@@ -428,6 +428,7 @@ mla::ProjArgs proj_args(const void* w0, const void* w1, int n_split, const void*
   a.w0 = (const uint16_t*)w0;
   a.w1 = (const uint16_t*)w1;
   a.n_split = n_split;
+  a.n_cache = n_split;
   a.ldw = K;
   a.x = x;
   a.ldx = K;
@@ -477,6 +478,78 @@ int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void
   mla::ProjArgs a = proj_args(W_DQ, W_DQ, d_q, h, B, d_q, D);
   a.y = c_q;
   a.ldy = d_q;
+  hipError_t e = mla::launch_proj(a, false, true, (float*)workspace, s);
+  if (e != hipSuccess) return hip_status(e);
+  // [q_C ; q_R] = [W_UQ ; W_QR] c_q, the q_R rows rotated at pos
+  mla::ProjArgs u = proj_args(W_UQ, W_QR, H * d_h, c_q, B, (int)n2, d_q);
+  u.y = q_C;
+  u.ldy = (int64_t)H * d_h;
+  u.y1 = q_R;
+  u.ldy1 = (int64_t)H * d_R;
+  u.pos = pos;
+  u.rope_base = rope_base;
+  return hip_status(mla::launch_proj(u, false, true, (float*)workspace, s));
+}
+
+size_t mla_query_append_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R, int d_c) {
+  if (B < 1 || D < 1 || d_q < 1 || H < 1 || d_h < 1 || d_R < 1 || d_c < 1) return 0;
+  const size_t a = mla::proj_ws_bytes(B, d_q + d_c + d_R, D);
+  const size_t b = mla::proj_ws_bytes(B, H * (d_h + d_R), d_q);
+  return a > b ? a : b;
+}
+
+int mla_query_proj_append(const void* h, const void* W_DQ, const void* W_UQ, const void* W_QR, const void* W_DKV,
+                          const void* W_KR, int dtype, const int32_t* pos, const mla_cache_desc* cache, int B, int D,
+                          int d_q, int H, int d_h, int d_R, int d_c, float rope_base, void* c_q, void* q_C, void* q_R,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || D < 1 || d_q < 1 || H < 1 || d_h < 1 || d_R < 1 || d_c < 1) return MLA_ERR_SHAPE;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(rope_base) || !(rope_base > 0.f)) return MLA_ERR_SHAPE;
+  if (!cache) return MLA_ERR_NULL;
+  if (!known_dtype(cache->latent_dtype) || !known_dtype(cache->rope_dtype)) return MLA_ERR_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!h || !W_DQ || !W_UQ || !W_QR || !W_DKV || !W_KR || !pos || !c_q || !q_C || !q_R || !cache->latent ||
+      !cache->rope)
+    return MLA_ERR_NULL;
+  if (dtype != MLA_BF16 || cache->latent_dtype != MLA_BF16 || cache->rope_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  const int64_t n2 = (int64_t)H * (d_h + d_R);
+  if (d_R != 64 || d_c != 512 || (d_h % 2) != 0 || ((H * d_h) % 8) != 0 || !proj_shape_ok(d_q, D) ||
+      !proj_shape_ok(d_q + d_c + d_R, D) || n2 > (1 << 30) || !proj_shape_ok((int)n2, d_q) || !proj_x_fits(B, D, 2) ||
+      B > 65535)
+    return MLA_ERR_UNSUPPORTED;
+  const bool paged = cache->block_table != nullptr;
+  if (cache->latent_stride_tok < 1 || cache->rope_stride_tok < 1 || cache->latent_stride_b < 0 ||
+      cache->rope_stride_b < 0)
+    return MLA_ERR_SHAPE;
+  if (paged && (cache->page_size < 1 || cache->max_pages < 1)) return MLA_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(W_DQ) || !aligned16(W_UQ) || !aligned16(W_QR) || !aligned16(W_DKV) ||
+      !aligned16(W_KR) || !aligned16(c_q) || !aligned16(q_C) || !aligned16(q_R) || !aligned16(cache->latent) ||
+      !aligned16(cache->rope) || ((cache->latent_stride_tok * 2) % 16) != 0 || ((cache->latent_stride_b * 2) % 16) != 0 ||
+      ((cache->rope_stride_tok * 2) % 16) != 0 || ((cache->rope_stride_b * 2) % 16) != 0)
+    return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla_query_append_workspace_bytes(B, D, d_q, H, d_h, d_R, d_c);
+  if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  // one pass over h: c_q = W_DQ h (to c_q), c = W_DKV h and RoPE_pos(W_KR h) (into the cache row)
+  mla::ProjArgs a = proj_args(W_DQ, W_KR, d_q + d_c, h, B, d_q + d_c + d_R, D);
+  a.y = c_q;
+  a.ldy = d_q;
+  a.pos = pos;
+  a.rope_base = rope_base;
+  a.dst_cache = 1;
+  a.wc = (const uint16_t*)W_DKV;
+  a.n_cache = d_q;
+  a.cache.latent = const_cast<void*>(cache->latent);
+  a.cache.rope = const_cast<void*>(cache->rope);
+  a.cache.block_table = cache->block_table;
+  a.cache.lat_sb = cache->latent_stride_b;
+  a.cache.lat_st = cache->latent_stride_tok;
+  a.cache.rope_sb = cache->rope_stride_b;
+  a.cache.rope_st = cache->rope_stride_tok;
+  a.cache.page_size = paged ? cache->page_size : 1;
+  a.cache.max_pages = paged ? cache->max_pages : 0;
+  a.cache.rope_base = rope_base;
   hipError_t e = mla::launch_proj(a, false, true, (float*)workspace, s);
   if (e != hipSuccess) return hip_status(e);
   // [q_C ; q_R] = [W_UQ ; W_QR] c_q, the q_R rows rotated at pos

@@ -59,7 +59,7 @@ __device__ __forceinline__ float2 rope_cs(const ProjArgs& a, int b, int n) {
 // the epilogue of one output pair (n, n + 1) of token b; cs is the pair's rotation when n >= n_split
 template <bool YBF16>
 __device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, float v0, float v1, float2 cs) {
-  if (a.dst_cache) {
+  if (a.dst_cache && n >= a.n_cache) {
     // the cache write: token b's new row at pos[b] (contiguous, or through the block table)
     const AppendArgs& c = a.cache;
     const int ps = a.pos[b];
@@ -74,7 +74,7 @@ __device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, floa
       rrow = (int64_t)b * c.rope_sb + (int64_t)ps * c.rope_st;
     }
     if (n < a.n_split)
-      *(uint32_t*)((uint16_t*)c.latent + lrow + n) = pack_bf16x2(v0, v1);
+      *(uint32_t*)((uint16_t*)c.latent + lrow + (n - a.n_cache)) = pack_bf16x2(v0, v1);
     else
       *(uint32_t*)((uint16_t*)c.rope + rrow + (n - a.n_split)) =
           pack_bf16x2(v0 * cs.x - v1 * cs.y, v0 * cs.y + v1 * cs.x);
@@ -96,7 +96,9 @@ __device__ __forceinline__ void store_pair(const ProjArgs& a, int b, int n, floa
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 
 __device__ __forceinline__ const uint16_t* wrow(const ProjArgs& a, int n) {
-  return n < a.n_split ? a.w0 + (int64_t)n * a.ldw : a.w1 + (int64_t)(n - a.n_split) * a.ldw;
+  if (n >= a.n_split) return a.w1 + (int64_t)(n - a.n_split) * a.ldw;
+  if (n >= a.n_cache) return a.wc + (int64_t)(n - a.n_cache) * a.ldw;
+  return a.w0 + (int64_t)n * a.ldw;
 }
 
 // 8 x-elements k .. k+7 of token b as bf16 pairs (fp32 x is rounded, for the MFMA operand)

@@ -19,7 +19,9 @@ struct AppendArgs {
 
 // projections y[b, n] = sum_k W[n, k] x[b, k] (proj.hip).  Rows n < n_split come from w0 and are
 // scaled and stored to y; rows n >= n_split come from w1 (row n - n_split) and are the rotary rows,
-// turned per 64-row head block at pos[b] and stored to y1 as bf16.  N % 32 == 0, K % 512 == 0.
+// turned per 64-row head block at pos[b] and stored to y1 as bf16.  With dst_cache, rows
+// [n_cache, n_split) come from wc and both they and the rotary rows go into the new token's cache
+// row instead.  N % 32 == 0, K % 512 == 0, segment boundaries even.
 constexpr int kProjGemvMaxB = 8;   // the GEMV kernel serves at most this many tokens
 // GEMV (no workspace) for up to 4 tokens, and for up to 8 when K is long (>= 4096); otherwise the
 // MFMA path (whose 32-token tile costs about the same from 1 to 32 tokens) is faster
@@ -39,8 +41,10 @@ struct ProjArgs {
   int64_t ldy1;
   const int32_t* pos;           // [B] positions of the rotary rows
   float rope_base;
-  int dst_cache;                // 1: rows < n_split go to the cache latent row of token b at pos[b],
-  AppendArgs cache;             //    the rotated rows to its rope row (bf16; y, y1 unused)
+  int dst_cache;                // 1: rows [n_cache, n_split) come from wc (row n - n_cache) and go to
+  AppendArgs cache;             //    the cache latent row of token b at pos[b], the rotated rows to its
+  const uint16_t* wc;           //    rope row (bf16; y1 unused); rows below n_cache still go to y
+  int n_cache;                  // == n_split unless dst_cache
 };
 // MFMA path (otherwise): workgroup tiles of 128 rows x up to 128 tokens; K is split into
 // proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups

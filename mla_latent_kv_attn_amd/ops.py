@@ -308,6 +308,40 @@ def mla_query_proj(h: torch.Tensor, W_DQ: torch.Tensor, W_UQ: torch.Tensor, W_QR
     return c_q, q_C, q_R
 
 
+def mla_query_append_workspace_bytes(B: int, D: int, d_q: int, H: int, d_h: int, d_R: int, d_c: int) -> int:
+    return int(_lib.lib().mla_query_append_workspace_bytes(B, D, d_q, H, d_h, d_R, d_c))
+
+
+def mla_query_proj_append(h: torch.Tensor, W_DQ: torch.Tensor, W_UQ: torch.Tensor, W_QR: torch.Tensor,
+                          W_DKV: torch.Tensor, W_KR: torch.Tensor, pos: torch.Tensor, cache: Cache, H: int,
+                          rope_base: float = 10000.0, c_q: Optional[torch.Tensor] = None,
+                          q_C: Optional[torch.Tensor] = None, q_R: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """mla_query_proj and mla_cache_append of the same tokens in two projections (bf16 caches).
+    Returns (c_q, q_C, q_R) as mla_query_proj; the cache row pos[b] is written as mla_cache_append."""
+    _dev(h, W_DQ, W_UQ, W_QR, W_DKV, W_KR, pos, c_q, q_C, q_R, workspace)
+    _contig(h=h, W_DQ=W_DQ, W_UQ=W_UQ, W_QR=W_QR, W_DKV=W_DKV, W_KR=W_KR, pos=pos, c_q=c_q, q_C=q_C, q_R=q_R)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos is int32")
+    B, D = h.shape
+    d_q, d_c, d_R = W_DQ.shape[0], W_DKV.shape[0], W_KR.shape[0]
+    d_h = W_UQ.shape[0] // H
+    if W_QR.shape[0] != H * d_R:
+        raise ValueError("W_QR rows must be H * d_R (the rope width of W_KR)")
+    if c_q is None:
+        c_q = torch.empty(B, d_q, dtype=torch.bfloat16, device=h.device)
+    if q_C is None:
+        q_C = torch.empty(B, H, d_h, dtype=torch.bfloat16, device=h.device)
+    if q_R is None:
+        q_R = torch.empty(B, H, d_R, dtype=torch.bfloat16, device=h.device)
+    wp, wn = _ws(mla_query_append_workspace_bytes(B, D, d_q, H, d_h, d_R, d_c), h, workspace, stream)
+    check("mla_query_proj_append", _lib.lib().mla_query_proj_append(
+        h.data_ptr(), W_DQ.data_ptr(), W_UQ.data_ptr(), W_QR.data_ptr(), W_DKV.data_ptr(), W_KR.data_ptr(),
+        dtype_code(h), pos.data_ptr(), ctypes.byref(cache.desc), B, D, d_q, H, d_h, d_R, d_c, float(rope_base),
+        c_q.data_ptr(), q_C.data_ptr(), q_R.data_ptr(), wp, wn, _stream(stream, h)))
+    return c_q, q_C, q_R
+
+
 def mla_fold_q(W_UQ: torch.Tensor, W_UK: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
     """W_QK[h] = W_UK[h]^T W_UQ[h d_h:(h+1) d_h]: W_UQ [H d_h, d_q], W_UK [H, d_h, d_c] -> [H, d_c, d_q] bf16."""
     _dev(W_UQ, W_UK, out)

@@ -297,3 +297,27 @@ def test_fold_and_out_proj_validation(lib):
     assert op(FAKE + 4, FAKE, L.MLA_BF16, FAKE, 1, 7168, 16384, None, 0, None) == L.MLA_ERR_UNSUPPORTED
     assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 9, 7168, 16384, None, 0, None) == L.MLA_ERR_WORKSPACE
     assert op(FAKE, FAKE, L.MLA_BF16, FAKE, 16384, 7168, 65536, FAKE, 1 << 40, None) == L.MLA_ERR_UNSUPPORTED
+
+
+def test_query_proj_append_validation(lib):
+    f = lib.mla_query_proj_append
+    ws = lib.mla_query_append_workspace_bytes
+    assert ws(1, 7168, 1536, 128, 128, 64, 512) == 0                          # GEMV passes
+    assert ws(64, 7168, 1536, 128, 128, 64, 512) == max(
+        lib.mla_proj_workspace_bytes(64, 1536 + 576, 7168), lib.mla_proj_workspace_bytes(64, 128 * 192, 1536))
+
+    def call(desc, B=1, dtype=L.MLA_BF16, d_c=512, d_R=64, pos=FAKE, wsp=None, wsb=0):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dtype, pos, ctypes.byref(desc), B, 7168, 1536, 128, 128, d_R, d_c,
+                 1e4, FAKE, FAKE, FAKE, wsp, wsb, None)
+
+    d = _desc()
+    assert call(d, B=-1) == L.MLA_ERR_SHAPE
+    assert call(d, dtype=7) == L.MLA_ERR_DTYPE
+    assert call(d, B=0, pos=None) == L.MLA_OK
+    assert call(d, pos=None) == L.MLA_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.MLA_BF16, FAKE, None, 1, 7168, 1536, 128, 128, 64, 512, 1e4, FAKE,
+             FAKE, FAKE, None, 0, None) == L.MLA_ERR_NULL
+    assert call(_desc(latent_dtype=L.MLA_FP8_E4M3)) == L.MLA_ERR_UNSUPPORTED   # E4M3: the two separate calls
+    assert call(d, d_c=256) == L.MLA_ERR_UNSUPPORTED
+    assert call(_desc(st_tok=577)) == L.MLA_ERR_UNSUPPORTED
+    assert call(d, B=64) == L.MLA_ERR_WORKSPACE

@@ -119,3 +119,35 @@ def test_decode_layer_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(layer.y, eager), f"replay {rep} differs from the eager layer"
         assert torch.isfinite(junk)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 12])
+def test_query_proj_append_matches_separate_calls(B):
+    # one pass over [W_DQ; W_DKV; W_KR] against mla_cache_append + mla_query_proj on a copy of the
+    # cache: bitwise up to 8 tokens (the same projection kernel per row); beyond, c_q / q_C / q_R
+    # bitwise and the cache row within one bf16 step (the separate cache write sums in another order)
+    print(f"mla_query_proj_append B={B}", flush=True)
+    rng = np.random.default_rng(60 + B)
+    lens = rng.integers(0, 120, size=B)
+    cap = 128
+    inp = make_layer_inputs(lens, cap, seed=61 + B)
+    w = {k: _dev(v) for k, v in inp.weights.items()}
+    h = _dev(inp.h)
+    pos = torch.from_numpy(inp.pos).cuda()
+    lat_a, rope_a = _dev(inp.latent), _dev(inp.rope)
+    lat_b, rope_b = lat_a.clone(), rope_a.clone()
+    fused = ops.mla_query_proj_append(h, w["W_DQ"], w["W_UQ"], w["W_QR"], w["W_DKV"], w["W_KR"], pos,
+                                      ops.Cache.split(lat_a, rope_a), H)
+    ops.mla_cache_append(h, w["W_DKV"], w["W_KR"], pos, ops.Cache.split(lat_b, rope_b))
+    sep = ops.mla_query_proj(h, w["W_DQ"], w["W_UQ"], w["W_QR"], pos, H)
+    torch.cuda.synchronize()
+    for x, y in zip(fused, sep):
+        assert np.array_equal(_bits(x), _bits(y))
+    if B <= 8:
+        assert np.array_equal(_bits(lat_a), _bits(lat_b)) and np.array_equal(_bits(rope_a), _bits(rope_b))
+    else:
+        for a_, b_ in ((lat_a, lat_b), (rope_a, rope_b)):
+            ga, gb = decode_bf16(_bits(a_)), decode_bf16(_bits(b_))
+            same = np.isnan(ga) & np.isnan(gb)
+            step = np.exp2(np.floor(np.log2(np.maximum(np.abs(np.nan_to_num(gb)), 2.0 ** -126))) - 7)
+            assert np.all(same | (np.abs(ga - gb) <= step * 1.0001))
