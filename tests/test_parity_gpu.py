@@ -363,11 +363,12 @@ def test_padded_row_strides(cfg):
     compare(inp, got, oracle.decode(inp))
 
 
-@pytest.mark.parametrize("H,splits", [(128, 100), (128, 0), (64, 0), (32, 0)])
+@pytest.mark.parametrize("H,splits", [(128, 100), (128, 0), (128, 129), (128, 1000), (64, 0), (32, 0)])
 def test_large_batch_kernel_variants(H, splits):
     """Batches past the small-batch switch (more than 1024 tiles of 32 tokens) take the
-    large-batch kernel: 128 heads in one workgroup (4 waves), in two head groups when there are
-    at most 128 splits, and the 64- and 32-head variants.  Sampled comparison."""
+    large-batch kernel: 128 heads in one workgroup (4 waves) with more than 128 splits (129 and
+    1000 requested: more splits than tiles leave workgroups idle), in two head groups when there
+    are at most 128, and the 64- and 32-head variants.  Sampled comparison."""
     B, n_max = 40, 1100
     wl = WORKLOADS[3].with_(name=f"large-h{H}-s{splits}", B=B, H=H, n_max=n_max, len_lo=1, len_hi=n_max)
     rng = np.random.default_rng(11)
@@ -378,4 +379,27 @@ def test_large_batch_kernel_variants(H, splits):
     all_finite(got, inp)
     pairs = _sample_pairs(inp)
     ref = oracle.decode(inp, pairs=pairs)
+    compare(inp, got, ref, pairs=pairs)
+
+
+def test_rising_scores_force_rescales_large_batch():
+    """As test_rising_scores_force_rescales, on a batch past the small-batch switch (the
+    large-batch kernel, 128 heads per workgroup): the rope keys grow with the token index, so
+    every segment's running maximum keeps rising and its accumulator is rescaled many times.
+    Sampled comparison."""
+    B, n_max = 40, 1100
+    wl = WORKLOADS[3].with_(name="large-rising", B=B, n_max=n_max, len_lo=1, len_hi=n_max, layout="split")
+    rng = np.random.default_rng(12)
+    lens = rng.integers(600, n_max + 1, size=B)
+    lens[:3] = [n_max, 1, 65]
+    inp = make_inputs(wl, lens=lens)
+    rope = bf16_bits_to_f32(inp.rope).reshape(B, n_max, 64)
+    grow = (1.0 + np.arange(n_max, dtype=np.float32) / 32.0)[None, :, None]
+    inp.rope = f32_to_bf16_bits(rope * grow).reshape(inp.rope.shape)
+    got = run_gpu(inp)
+    all_finite(got, inp)
+    pairs = _sample_pairs(inp)
+    ref = oracle.decode(inp, pairs=pairs)
+    nonempty = [(b, h) for b, h in pairs if lens[b] > 64]
+    assert float(np.median([ref["lse"][b, h] for b, h in nonempty])) > 25.0
     compare(inp, got, ref, pairs=pairs)
