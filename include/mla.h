@@ -337,7 +337,8 @@ int mla_query_proj(const void* h, const void* W_DQ, const void* W_UQ, const void
  * cache must be bf16 (latent and rope; E4M3 caches need the row's amax first: use the two
  * calls).  workspace: at least mla_query_append_workspace_bytes(B, D, d_q, H, d_h, d_R, d_c)
  * bytes (NULL allowed when 0).  Up to 8 tokens the results are bitwise those of the two separate
- * calls; beyond, c_q, q_C and q_R still are, and the cache row is the same sums in another order.
+ * calls (the same per-row kernel); beyond, every output is the same sums split into other K
+ * chunks (the stacked rows are a different projection shape), equal up to rounding.
  * Supported: dtype MLA_BF16, d_c == 512, d_R == 64, and mla_query_proj's shape rules.
  */
 size_t mla_query_append_workspace_bytes(int B, int D, int d_q, int H, int d_h, int d_R, int d_c);

@@ -222,9 +222,11 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
 // MFMA, B > 8.  grid (ceil(N / 128), ceil(B / 128), chunks), 256 threads.  The workgroup owns rows
 // [128 x, 128 x + 128) (wave w: 32 of them) and tokens [128 y, 128 y + 32 NT) over chunk z of K
 // (kc elements).  Per 64-element step of K the tokens' x (rounded to bf16) goes through LDS once
-// for all four waves (double buffered, one barrier per step), while each wave loads its rows'
-// W for the next step straight into registers in the MFMA operand layout (lane: row lane % 32,
-// 8 elements at 16 s + 8 (lane / 32)).  A = x (tokens), B = W (rows), D[token][row] in fp32.
+// for all four waves (double buffered, one barrier per step; x is read from L2 one step ahead),
+// while each wave loads its rows' W straight into registers in the MFMA operand layout (lane:
+// row lane % 32, 8 elements at 16 s + 8 (lane / 32)), two steps ahead through a ring of three
+// register sets (the step loop is unrolled by three so that the ring indices are constants).
+// A = x (tokens), B = W (rows), D[token][row] in fp32.
 // ------------------------------------------------------------------------------------------------
 template <int NT, bool XF32>
 __global__ __launch_bounds__(256) void k_proj_mfma(ProjArgs a, int kc, float* __restrict__ part) {
@@ -256,33 +258,40 @@ __global__ __launch_bounds__(256) void k_proj_mfma(ProjArgs a, int kc, float* __
       *(u32x4*)&xs[buf][(piece >> 3) * kRowB + 16 * (piece & 7)] = xr[i];
     }
   };
-  u32x4 wr[2][4];
+  // inactive waves (rows past N) read row 0 (in bounds) and store nothing
+  u32x4 wr[3][4];
   auto load_w = [&](int k, u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = active ? *(const u32x4*)(w + (k - kbeg) + 16 * s) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < 4; ++s) dst[s] = *(const u32x4*)(w + (k - kbeg) + 16 * s);
   };
 
   f32x16 acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x16{};
   const int nsteps = kc / kStep;
+  // Every load is unconditional (steps past the chunk's end reread its last step, from L2): a load
+  // under a branch makes the compiler's wait counting fall back to waiting for all loads in flight
+  // where the paths join, which would undo the prefetch.  Inactive waves compute on row 0 and
+  // store nothing.
   load_x(kbeg);
   load_w(kbeg, wr[0]);
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    store_x(buf);
-    __syncthreads();
-    if (st + 1 < nsteps) {
-      load_x(kbeg + (st + 1) * kStep);
-      load_w(kbeg + (st + 1) * kStep, wr[buf ^ 1]);
-    }
-    if (active) {
+  load_w(kbeg + min(1, nsteps - 1) * kStep, wr[1]);
+  for (int st0 = 0; st0 < nsteps; st0 += 3) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int st = st0 + u;
+      if (st >= nsteps) break;
+      const int buf = st & 1;
+      store_x(buf);
+      __syncthreads();
+      load_x(kbeg + min(st + 1, nsteps - 1) * kStep);
+      load_w(kbeg + min(st + 2, nsteps - 1) * kStep, wr[(u + 2) % 3]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
           const u32x4 xa = *(const u32x4*)&xs[buf][(32 * i + (lane & 31)) * kRowB + 32 * s + 16 * (lane >> 5)];
-          acc[i] = mfma32x32x16(xa, wr[buf][s], acc[i]);
+          acc[i] = mfma32x32x16(xa, wr[u][s], acc[i]);
         }
       }
     }

@@ -47,13 +47,17 @@ struct ProjArgs {
   int n_cache;                  // == n_split unless dst_cache
 };
 // MFMA path (otherwise): workgroup tiles of 128 rows x up to 128 tokens; K is split into
-// proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 512 workgroups
+// proj_chunks(B, N, K) chunks, a divisor of K / 256, the fewest that give at least 224 workgroups
+// and at most 4096 elements of K per chunk (with W two steps ahead in every workgroup, about one
+// workgroup per CU keeps enough loads in flight; more chunks add partial sums without streaming
+// faster, and longer chunks leave the chip's second workgroup slot idle on the long rows of the
+// folded W_O W_UV)
 constexpr int kProjRows = 128, kProjToks = 128;
 inline int proj_chunks(int B, int N, int K) {
   const int64_t blocks = (int64_t)((N + kProjRows - 1) / kProjRows) * ((B + kProjToks - 1) / kProjToks);
   const int units = K / 256;
   for (int d = 1; d <= units; ++d)
-    if (units % d == 0 && blocks * d >= 512) return d;
+    if (units % d == 0 && blocks * d >= 224 && K / d <= 4096) return d;
   return units;
 }
 size_t proj_ws_bytes(int B, int N, int K);

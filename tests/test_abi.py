@@ -238,13 +238,15 @@ def test_projection_workspace_rules(lib):
     ws = lib.mla_proj_workspace_bytes
     # GEMV (no workspace): up to 4 tokens, or up to 8 with K >= 4096
     assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0 and ws(4, 24576, 1536) == 0
-    assert ws(5, 24576, 1536) == 3 * 5 * 24576 * 4                            # K < 4096: MFMA path
+    assert ws(5, 24576, 1536) == 2 * 5 * 24576 * 4                            # K < 4096: MFMA path
     # MFMA path: tiles of 128 rows x 128 tokens; K split into d chunks, d the smallest divisor of
-    # K / 256 that gives at least 512 workgroups (else K / 256)
+    # K / 256 that gives at least 224 workgroups and chunks of at most 4096 elements (else K / 256)
     assert ws(9, 1536, 7168) == 28 * 9 * 1536 * 4                             # 12 tiles: 28 chunks
-    assert ws(64, 24576, 1536) == 3 * 64 * 24576 * 4                          # 192 tiles: 3 chunks
-    assert ws(128, 7168, 16384) == 16 * 128 * 7168 * 4                        # 56 tiles: 16 chunks
-    assert ws(129, 7168, 16384) == 8 * 129 * 7168 * 4                         # 112 tiles: 8 chunks
+    assert ws(9, 2112, 7168) == 14 * 9 * 2112 * 4                             # 17 tiles: 14 chunks
+    assert ws(64, 24576, 1536) == 2 * 64 * 24576 * 4                          # 192 tiles: 2 chunks
+    assert ws(128, 7168, 16384) == 4 * 128 * 7168 * 4                         # 56 tiles: 4 chunks
+    assert ws(129, 7168, 16384) == 4 * 129 * 7168 * 4                         # 112 tiles: 4 chunks (<= 4096)
+    assert ws(64, 7168, 65536) == 16 * 64 * 7168 * 4                          # folded W_OV: 16 chunks
     assert ws(0, 32, 512) == 0
     q = lib.mla_query_workspace_bytes
     assert q(1, 7168, 1536, 128, 128, 64) == 0 and q(2, 7168, 1536, 128, 128, 64) == 0

@@ -121,11 +121,19 @@ def test_decode_layer_graph_replays_match_eager():
         assert torch.isfinite(junk)
 
 
-@pytest.mark.parametrize("B", [1, 3, 8, 12])
+def _within_bf16_step(a_bits, b_bits):
+    ga, gb = decode_bf16(a_bits), decode_bf16(b_bits)
+    same = np.isnan(ga) & np.isnan(gb)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(np.nan_to_num(gb)), 2.0 ** -126))) - 7)
+    return np.all(same | (np.abs(ga - gb) <= step * 1.0001))
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 12, 64])
 def test_query_proj_append_matches_separate_calls(B):
     # one pass over [W_DQ; W_DKV; W_KR] against mla_cache_append + mla_query_proj on a copy of the
-    # cache: bitwise up to 8 tokens (the same projection kernel per row); beyond, c_q / q_C / q_R
-    # bitwise and the cache row within one bf16 step (the separate cache write sums in another order)
+    # cache: bitwise up to 8 tokens (the same projection kernel per row); beyond, the fused pass
+    # splits K into other chunks than the separate calls (sums in another order): c_q and the cache
+    # row within one bf16 step, q_C / q_R (from that c_q) within relative L2 1e-3
     print(f"mla_query_proj_append B={B}", flush=True)
     rng = np.random.default_rng(60 + B)
     lens = rng.integers(0, 120, size=B)
@@ -141,13 +149,13 @@ def test_query_proj_append_matches_separate_calls(B):
     ops.mla_cache_append(h, w["W_DKV"], w["W_KR"], pos, ops.Cache.split(lat_b, rope_b))
     sep = ops.mla_query_proj(h, w["W_DQ"], w["W_UQ"], w["W_QR"], pos, H)
     torch.cuda.synchronize()
-    for x, y in zip(fused, sep):
-        assert np.array_equal(_bits(x), _bits(y))
     if B <= 8:
+        for x, y in zip(fused, sep):
+            assert np.array_equal(_bits(x), _bits(y))
         assert np.array_equal(_bits(lat_a), _bits(lat_b)) and np.array_equal(_bits(rope_a), _bits(rope_b))
     else:
+        assert _within_bf16_step(_bits(fused[0]), _bits(sep[0]))
+        for x, y in zip(fused[1:], sep[1:]):
+            assert relative_l2(decode_bf16(_bits(x)).astype(np.float64), decode_bf16(_bits(y)).astype(np.float64)) <= 1e-3
         for a_, b_ in ((lat_a, lat_b), (rope_a, rope_b)):
-            ga, gb = decode_bf16(_bits(a_)), decode_bf16(_bits(b_))
-            same = np.isnan(ga) & np.isnan(gb)
-            step = np.exp2(np.floor(np.log2(np.maximum(np.abs(np.nan_to_num(gb)), 2.0 ** -126))) - 7)
-            assert np.all(same | (np.abs(ga - gb) <= step * 1.0001))
+            assert _within_bf16_step(_bits(a_), _bits(b_))
