@@ -294,7 +294,7 @@ int mla_mha_decode(const void* q, const void* k_cache, const void* v_cache, int 
 /*
  * Projections around the attention core.  Each is y[b, n] = sum_k W[n, k] x[b, k] over a bf16
  * weight W [N, K] (row n maps x to output n, the column-vector form y = W x) with fp32
- * accumulation.  Up to 4 tokens, or up to 8 tokens when K >= 4096: a streaming GEMV, no
+ * accumulation.  Up to 4 tokens, or up to 8 tokens when K >= 4096 and N * K <= 32M: a streaming GEMV, no
  * workspace needed.  Otherwise: bf16 MFMA (fp32 x is rounded to bf16 for it) split over K, partial sums in
  * the workspace, added in a fixed order.  Deterministic.
  *

@@ -204,7 +204,9 @@ __global__ __launch_bounds__(256) void k_append_finalize(const float* __restrict
 
 hipError_t launch_append(const void* h, const void* w_dkv, const void* w_kr, const int32_t* pos, int B, int D,
                          const AppendArgs& a, bool fp8, bool paged, float* ws, hipStream_t s) {
-  if (!fp8 && B <= kProjGemvMaxB) {
+  // one pass only where the projection GEMV serves it (no workspace; the workspace of this call is
+  // sized for the two-pass form)
+  if (!fp8 && proj_uses_gemv(B, kOut, D)) {
     ProjArgs pa{};
     pa.w0 = (const uint16_t*)w_dkv;
     pa.wc = (const uint16_t*)w_dkv;

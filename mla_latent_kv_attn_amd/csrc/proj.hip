@@ -117,7 +117,7 @@ __device__ __forceinline__ u32x4 load_x_bf16(const ProjArgs& a, int b, int k) {
 }  // namespace
 
 size_t proj_ws_bytes(int B, int N, int K) {
-  if (proj_uses_gemv(B, K)) return 0;
+  if (proj_uses_gemv(B, N, K)) return 0;
   return (size_t)proj_chunks(B, N, K) * (size_t)B * (size_t)N * sizeof(float);
 }
 
@@ -418,7 +418,7 @@ hipError_t launch_gemv_nb(const ProjArgs& a, hipStream_t s) {
 
 template <bool XF32, bool YBF16>
 hipError_t launch_proj_t(const ProjArgs& a, float* ws, hipStream_t s) {
-  if (proj_uses_gemv(a.B, a.K)) return launch_gemv_nb<XF32, YBF16>(a, s);
+  if (proj_uses_gemv(a.B, a.N, a.K)) return launch_gemv_nb<XF32, YBF16>(a, s);
   const int nz = proj_chunks(a.B, a.N, a.K);
   const dim3 grid((a.N + kProjRows - 1) / kProjRows, (a.B + kProjToks - 1) / kProjToks, nz);
   const int toks = a.B < kProjToks ? a.B : kProjToks;     // tokens of the widest workgroup

@@ -23,9 +23,12 @@ struct AppendArgs {
 // [n_cache, n_split) come from wc and both they and the rotary rows go into the new token's cache
 // row instead.  N % 32 == 0, K % 512 == 0, segment boundaries even.
 constexpr int kProjGemvMaxB = 8;   // the GEMV kernel serves at most this many tokens
-// GEMV (no workspace) for up to 4 tokens, and for up to 8 when K is long (>= 4096); otherwise the
-// MFMA path (whose 32-token tile costs about the same from 1 to 32 tokens) is faster
-inline bool proj_uses_gemv(int B, int K) { return B <= 4 || (B <= kProjGemvMaxB && K >= 4096); }
+// GEMV (no workspace) for up to 4 tokens, and for up to 8 when K is long (>= 4096) and the weight
+// small (at most 32M elements: W_DQ, the cache write); otherwise the MFMA path (whose 32-token tile
+// costs about the same from 1 to 32 tokens, with W two steps ahead) is faster
+inline bool proj_uses_gemv(int B, int N, int K) {
+  return B <= 4 || (B <= kProjGemvMaxB && K >= 4096 && (int64_t)N * K <= ((int64_t)32 << 20));
+}
 struct ProjArgs {
   const uint16_t* w0;
   const uint16_t* w1;

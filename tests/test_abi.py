@@ -236,8 +236,10 @@ def test_mha_decode_validation(lib):
 
 def test_projection_workspace_rules(lib):
     ws = lib.mla_proj_workspace_bytes
-    # GEMV (no workspace): up to 4 tokens, or up to 8 with K >= 4096
-    assert ws(1, 1536, 7168) == 0 and ws(8, 7168, 16384) == 0 and ws(4, 24576, 1536) == 0
+    # GEMV (no workspace): up to 4 tokens, or up to 8 with K >= 4096 and at most 32M weight elements
+    assert ws(1, 1536, 7168) == 0 and ws(4, 7168, 16384) == 0 and ws(4, 24576, 1536) == 0
+    assert ws(8, 1536, 7168) == 0 and ws(8, 2112, 7168) == 0 and ws(8, 576, 7168) == 0
+    assert ws(8, 7168, 16384) == 4 * 8 * 7168 * 4                            # W_O at 5-8 tokens: MFMA
     assert ws(5, 24576, 1536) == 2 * 5 * 24576 * 4                            # K < 4096: MFMA path
     # MFMA path: tiles of 128 rows x 128 tokens; K split into d chunks, d the smallest divisor of
     # K / 256 that gives at least 224 workgroups and chunks of at most 4096 elements (else K / 256)

@@ -178,3 +178,25 @@ def test_append_zero_hidden_state_and_large_positions():
     sc = torch.full((B, N), SENTF, dtype=torch.float32, device="cuda")
     _run(Cache.split(lat8, rope, sc), inp, pos, B)
     assert float(sc[0, 5]) == 1.0 and int(lat8[0, 5].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("B,Dm", [(6, 1024), (3, 1024), (8, 2048)])
+def test_append_short_rows(B, Dm):
+    """A model width below 4096 at 5-8 tokens takes the two-pass form (the one-pass form is kept for
+    the projection GEMV, which needs no workspace); at 3 tokens the GEMV serves the short rows."""
+    from mla_latent_kv_attn_amd.ops import Cache
+    N = 40
+    inp = make_append_inputs(B, Dm, seed=200 + B)
+    pos = (np.arange(B) * 7) % N
+    lat0 = np.full((B, N, DC), SENT16, dtype=np.uint16)
+    rope0 = np.full((B, N, DR), SENT16, dtype=np.uint16)
+    lat, rope = _bf16_tensor(lat0), _bf16_tensor(rope0)
+    _run(Cache.split(lat, rope), inp, pos, B)
+    ref = _oracle(inp, pos)
+    lat_g, rope_g = _bits(lat), _bits(rope)
+    rows = (np.arange(B), pos)
+    mask = np.ones((B, N), bool)
+    mask[rows] = False
+    assert np.array_equal(lat_g[mask], lat0[mask]) and np.array_equal(rope_g[mask], rope0[mask])
+    _check_bf16(lat_g[rows], ref["c"], "latent")
+    _check_bf16(rope_g[rows], ref["k_R"], "rope")

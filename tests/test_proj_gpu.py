@@ -184,7 +184,9 @@ def test_out_proj_v3(v3_output, B):
     got = ops.mla_out_proj(torch.from_numpy(x).cuda(), dW_O)
     torch.cuda.synchronize()
     ref = oo.out_proj(W_O, x)
-    tol = 2e-5 if B <= 8 else 4e-3
+    # the GEMV (fp32 x, fp32 sums) serves W_O up to 4 tokens; from 5 (W_O has more than 32M
+    # elements) the MFMA path rounds x to bf16
+    tol = 2e-5 if B <= 4 else 4e-3
     assert relative_l2(got.cpu().numpy().astype(np.float64), ref) <= tol
 
 
