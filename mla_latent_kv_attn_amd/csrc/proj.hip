@@ -48,12 +48,14 @@ __device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v 
 
 // rotation of the rotary pair that holds output n (n >= n_split) of token b: cos and sin of
 // pos[b] * base^(-2i/64), i the pair index within the head, in double precision
-__device__ __forceinline__ float2 rope_cs(const ProjArgs& a, int b, int n) {
-  const int i = ((n - a.n_split) % kRot) >> 1;
+__device__ __forceinline__ float2 rope_cs_pair(const ProjArgs& a, int b, int i) {
   const double th = (double)a.pos[b] * pow((double)a.rope_base, -2.0 * i / (double)kRot);
   double sn, cs;
   sincos(th, &sn, &cs);
   return make_float2((float)cs, (float)sn);
+}
+__device__ __forceinline__ float2 rope_cs(const ProjArgs& a, int b, int n) {
+  return rope_cs_pair(a, b, ((n - a.n_split) % kRot) >> 1);
 }
 
 // the epilogue of one output pair (n, n + 1) of token b; cs is the pair's rotation when n >= n_split
@@ -308,27 +310,43 @@ __global__ __launch_bounds__(256) void k_proj_mfma(ProjArgs a, int kc, float* __
     }
 }
 
-// grid (ceil(N / 512), B), 256 threads: thread t owns outputs 2t, 2t + 1 of its 512-row block
-template <bool YBF16>
+// grid (ceil(N / 1024), B), 256 threads: thread t owns outputs 4t .. 4t + 3 (two pairs) of its
+// 1024-row block (N % 4 == 0).  The chunks' partials are read G at a time (16 bytes each, every
+// load unconditional: chunk indices past nz are clamped and their values not added) and summed in
+// chunk order.
+template <bool YBF16, int G>
 __global__ __launch_bounds__(256) void k_proj_reduce(ProjArgs a, int nz, const float* __restrict__ part) {
   const int b = blockIdx.y;
-  const int n = blockIdx.x * 512 + 2 * threadIdx.x;
+  const int n = blockIdx.x * 1024 + 4 * threadIdx.x;
+  // every head block of token b turns its rotary pairs by the same kRot / 2 angles: computed once
+  // per workgroup (the same double-precision function as elsewhere, so the same values)
+  __shared__ float2 cs_s[kRot / 2];
+  const bool rot = a.N > a.n_split && (int)blockIdx.x * 1024 + 1024 > a.n_split;   // workgroup-uniform
+  if (rot) {
+    if (threadIdx.x < kRot / 2) cs_s[threadIdx.x] = rope_cs_pair(a, b, threadIdx.x);
+    __syncthreads();
+  }
   if (n >= a.N) return;
   const float* p = part + (int64_t)b * a.N + n;
   const int64_t zs = (int64_t)a.B * a.N;
-  float v0 = 0.f, v1 = 0.f;
-  for (int z0 = 0; z0 < nz; z0 += 8) {                  // groups of 8 loads in flight, summed in order
-    float2 u[8];
+  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  for (int z0 = 0; z0 < nz; z0 += G) {
+    f32x4 u[G];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = *(const float2*)(p + min(z0 + i, nz - 1) * zs);
+    for (int i = 0; i < G; ++i) u[i] = *(const f32x4*)(p + min(z0 + i, nz - 1) * zs);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < G; ++i)
       if (z0 + i < nz) {
-        v0 += u[i].x;
-        v1 += u[i].y;
+        v0 += u[i][0];
+        v1 += u[i][1];
+        v2 += u[i][2];
+        v3 += u[i][3];
       }
   }
-  store_pair<YBF16>(a, b, n, v0, v1, n >= a.n_split ? rope_cs(a, b, n) : make_float2(1.f, 0.f));
+  const int i0 = n >= a.n_split ? ((n - a.n_split) % kRot) >> 1 : 0;
+  const int i1 = n + 2 >= a.n_split ? ((n + 2 - a.n_split) % kRot) >> 1 : 0;
+  store_pair<YBF16>(a, b, n, v0, v1, n >= a.n_split ? cs_s[i0] : make_float2(1.f, 0.f));
+  store_pair<YBF16>(a, b, n + 2, v2, v3, n + 2 >= a.n_split ? cs_s[i1] : make_float2(1.f, 0.f));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -430,8 +448,13 @@ hipError_t launch_proj_t(const ProjArgs& a, float* ws, hipStream_t s) {
     hipLaunchKernelGGL((k_proj_mfma<4, XF32>), grid, dim3(256), 0, s, a, a.K / nz, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_proj_reduce<YBF16>), dim3((a.N + 511) / 512, a.B), dim3(256), 0, s, a, nz,
-                     (const float*)ws);
+  const dim3 rg((a.N + 1023) / 1024, a.B);
+  if (nz <= 2)
+    hipLaunchKernelGGL((k_proj_reduce<YBF16, 2>), rg, dim3(256), 0, s, a, nz, (const float*)ws);
+  else if (nz <= 4)
+    hipLaunchKernelGGL((k_proj_reduce<YBF16, 4>), rg, dim3(256), 0, s, a, nz, (const float*)ws);
+  else
+    hipLaunchKernelGGL((k_proj_reduce<YBF16, 8>), rg, dim3(256), 0, s, a, nz, (const float*)ws);
   return hipGetLastError();
 }
 }  // namespace
