@@ -101,6 +101,7 @@ def test_decode_attn_validation(lib):
     assert _attn(lib, d, max_len=-5) == L.MLA_ERR_SHAPE
     assert _attn(lib, d, scale=float("nan")) == L.MLA_ERR_SHAPE
     assert _attn(lib, d, B=3000) == L.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, d, B=2049) == L.MLA_ERR_UNSUPPORTED                # the batch limit is 2048
     assert _attn(lib, None) == L.MLA_ERR_NULL
     assert _attn(lib, d, q_dtype=7) == L.MLA_ERR_DTYPE
     assert _attn(lib, _desc(latent_dtype=5)) == L.MLA_ERR_DTYPE

@@ -403,3 +403,33 @@ def test_rising_scores_force_rescales_large_batch():
     nonempty = [(b, h) for b, h in pairs if lens[b] > 64]
     assert float(np.median([ref["lse"][b, h] for b, h in nonempty])) > 25.0
     compare(inp, got, ref, pairs=pairs)
+
+
+def test_max_batch_sampled():
+    """The library's batch limit (2048 sequences) with short ragged lengths, empty sequences among
+    them: the large-batch kernel's tile prefix and the combine at their widest.  Sampled pairs."""
+    B, n_max = 2048, 40
+    wl = WORKLOADS[2].with_(name="max-batch", B=B, n_max=n_max, len_lo=0, len_hi=n_max)
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, n_max + 1, size=B)
+    lens[:3] = [n_max, 0, 1]
+    inp = make_inputs(wl, lens=lens)
+    got = run_gpu(inp)
+    all_finite(got, inp)
+    pairs = _sample_pairs(inp, n_b=10)
+    ref = oracle.decode(inp, pairs=pairs)
+    compare(inp, got, ref, pairs=pairs)
+
+
+def test_long_sequence_sampled():
+    """One sequence of 131072 tokens: past the small-batch switch at one sequence (the large-batch
+    kernel over 256 splits), through the separate combine and through the decode step's fused
+    combine + W_UV (256 segments per head).  Sampled heads."""
+    n = 131072
+    wl = WORKLOADS[2].with_(name="long-131k", B=1, n_max=n, len_lo=n, len_hi=n)
+    inp = make_inputs(wl)
+    pairs = [(0, 0), (0, 77), (0, 127)]
+    ref = oracle.decode(inp, pairs=pairs)
+    for got in (run_gpu(inp), run_step(inp)):
+        all_finite(got, inp)
+        compare(inp, got, ref, pairs=pairs)
