@@ -10,7 +10,7 @@
 //
 // For the few tokens of a decode step every weight byte is used B times, so the work is a
 // stream of the weights from HBM.  Two kernels (the GEMV for up to 4 tokens, and for up to 8 when
-// K >= 4096; the MFMA path otherwise):
+// K >= 4096 and the weight has at most 32M elements; the MFMA path otherwise):
 //  * k_proj_gemv: one workgroup (4 waves) per R rows of W (R = 2, 4 or 8 by batch) over
 //    the whole of K.  K is cut into 512-element chunks; wave w takes chunks w, w + 4, ... with U
 //    chunks' loads in flight together.  Lane l reads elements 8l .. 8l+7 of a chunk of each of the
@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// MFMA, B > 8.  grid (ceil(N / 128), ceil(B / 128), chunks), 256 threads.  The workgroup owns rows
+// MFMA, the batches the GEMV does not serve.  grid (ceil(N / 128), ceil(B / 128), chunks), 256
+// threads.  The workgroup owns rows
 // [128 x, 128 x + 128) (wave w: 32 of them) and tokens [128 y, 128 y + 32 NT) over chunk z of K
 // (kc elements).  Per 64-element step of K the tokens' x (rounded to bf16) goes through LDS once
 // for all four waves (double buffered, one barrier per step; x is read from L2 one step ahead),
