@@ -82,6 +82,9 @@ def parse():
                     help="--row layer: tokens per sequence after the new one is appended")
     ap.add_argument("--append-batch", type=int, default=1,
                     help="--row append / query / out: new tokens (sequences) per call")
+    ap.add_argument("--shard", type=int, default=1, metavar="G",
+                    help="decode row: one GPU's share of the workload split by token range over G GPUs "
+                         "(every sequence keeps 1/G of its tokens); the exchange between GPUs is not run")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
     return ap.parse_args()
@@ -201,6 +204,11 @@ def main():
     from workloads.device import device_cache, to_device
 
     wl = WORKLOADS[args.config]
+    if args.shard > 1:
+        G = args.shard
+        wl = wl.with_(name=f"{wl.name}-shard{G}", n_max=wl.n_max // G, len_lo=max(1, wl.len_lo // G),
+                      len_hi=wl.len_hi // G,
+                      description=f"{wl.description}; one GPU's share of {G} by token range (tokens / {G})")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
