@@ -31,7 +31,13 @@
  *  - Values held in device memory (sequence lengths, block-table entries) are
  *    not validated: a length above max_len or outside the cache capacity, or a
  *    page id outside the pool, is undefined behaviour.
- *  - Results are bitwise reproducible for fixed arguments (no atomics).
+ *  - Results are bitwise reproducible for fixed arguments: every sum is taken in a fixed order.
+ *    Some kernels exchange data between workgroups of one launch (mla_decode_combine_uv at
+ *    small batch): the producers write with device-coherent (agent-scope) stores, wait until
+ *    those stores have completed (s_waitcnt vmcnt(0)), then raise an agent-scope counter with
+ *    an integer atomic add; a consumer reads the data with device-coherent loads only after it
+ *    has seen the counter's final value, and adds the parts in a fixed order, so the result does
+ *    not depend on which workgroup finished last.  No floating-point atomics are used.
  *  - Calls on different streams are independent; the library keeps no state
  *    other than the per-thread last HIP error.
  */

@@ -386,3 +386,171 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except (AssertionError, ValueError):
             failures += 1
     assert failures >= 1, f"planted mistake {name!r} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# the error metric and the cache read, pinned by hand-computed cases
+# --------------------------------------------------------------------------
+def check_relative_l2_hand_cases():
+    """||x - ref||_2 / ||ref||_2, worked by hand."""
+    rl2 = od.relative_l2
+    # diff (0, 2, 2): norm sqrt(8); ref norm 1
+    assert rl2([1.0, 2.0, 2.0], [1.0, 0.0, 0.0]) == pytest.approx(math.sqrt(8.0), rel=1e-15)
+    # diff (0.1, 0): 0.1 / sqrt(2) -- a norm ratio, not the largest elementwise error (0.1)
+    assert rl2([1.1, 1.0], [1.0, 1.0]) == pytest.approx(0.1 / math.sqrt(2.0), rel=1e-12)
+    # diff (3, 4) over ref (6, 8): 5 / 10
+    assert rl2([9.0, 12.0], [6.0, 8.0]) == pytest.approx(0.5, rel=1e-15)
+    # NaN entries of the reference (pairs not computed) are skipped: diff (1, 0) over ref (1, 0)
+    assert rl2([2.0, 100.0, 0.0], [1.0, np.nan, 0.0]) == pytest.approx(1.0, rel=1e-15)
+    # a zero reference gives the absolute norm of x
+    assert rl2([3.0, 4.0], [0.0, 0.0]) == pytest.approx(5.0, rel=1e-15)
+    # identical arrays: exactly zero; 2-D arrays are flattened
+    assert rl2(np.ones((2, 3)), np.ones((2, 3))) == 0.0
+    assert rl2([[1.0, 0.0], [0.0, 0.0]], [[0.0, 0.0], [0.0, 2.0]]) == pytest.approx(math.sqrt(5.0) / 2.0, rel=1e-15)
+
+
+def test_relative_l2_hand_cases():
+    check_relative_l2_hand_cases()
+
+
+def _bf16_bits(vals):
+    """Bit patterns of values exactly representable in bfloat16 (small integers here), written
+    out from the float32 bit pattern; NaN -> 0x7FC0."""
+    out = []
+    for v in np.asarray(vals, dtype=np.float64).reshape(-1):
+        if math.isnan(v):
+            out.append(0x7FC0)
+        else:
+            u = int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+            assert u & 0xFFFF == 0, v
+            out.append(u >> 16)
+    return np.array(out, dtype=np.uint16).reshape(np.shape(vals))
+
+
+def _tiny_wl(layout, B, n_max, dtype="bf16", page_size=64):
+    from workloads.configs import Workload
+    return Workload("hand", seed=0, B=B, H=1, d_h=1, d_c=2, d_R=1, n_max=n_max, len_lo=0, len_hi=n_max,
+                    dtype=dtype, layout=layout, page_size=page_size)
+
+
+def check_gather_rows_hand_placed():
+    """Rows placed by hand in each cache layout; latent columns first, then the rope columns
+    ("MLA storage: Representing KV with a small latent vector", section "Storing a positional key
+    separately": a cached row is the latent followed by the rope key).  d_c = 2, d_R = 1."""
+    from workloads.gen import DecodeInputs
+    nan = float("nan")
+    z = np.zeros((2, 1, 1), dtype=np.uint16)
+    # packed [B=2, n_max=3, 3]: sequence 0 holds two tokens, sequence 1 three
+    kv = _bf16_bits([[[1, 2, 3], [4, 5, 6], [nan, nan, nan]],
+                     [[7, 8, 9], [10, 11, 12], [13, 14, 15]]])
+    pk = DecodeInputs(wl=_tiny_wl("packed", 2, 3), lens=np.array([2, 3], dtype=np.int32),
+                      q_C=z, q_R=z, W_UK=z, W_UV=z, kv=kv)
+    C, R = od.gather_rows(pk, 0)
+    np.testing.assert_array_equal(C, [[1, 2], [4, 5]])
+    np.testing.assert_array_equal(R, [[3], [6]])
+    C, R = od.gather_rows(pk, 1)
+    np.testing.assert_array_equal(C, [[7, 8], [10, 11], [13, 14]])
+    np.testing.assert_array_equal(R, [[9], [12], [15]])
+    # paged: pages of 2 tokens, block table [[3, 1], [0, 2]]; sequence 0 has 3 tokens (page 3
+    # slots 0, 1, then page 1 slot 0), sequence 1 has 2 (page 0 slots 0, 1); the rest is padding
+    pool = np.full((4, 2, 3), nan)
+    pool[3, 0] = [1, 2, 3]
+    pool[3, 1] = [4, 5, 6]
+    pool[1, 0] = [7, 8, 9]
+    pool[0, 0] = [10, 11, 12]
+    pool[0, 1] = [13, 14, 15]
+    pg = DecodeInputs(wl=_tiny_wl("paged", 2, 4, page_size=2), lens=np.array([3, 2], dtype=np.int32),
+                      q_C=z, q_R=z, W_UK=z, W_UV=z, pool=_bf16_bits(pool),
+                      block_table=np.array([[3, 1], [0, 2]], dtype=np.int32))
+    C, R = od.gather_rows(pg, 0)
+    np.testing.assert_array_equal(C, [[1, 2], [4, 5], [7, 8]])
+    np.testing.assert_array_equal(R, [[3], [6], [9]])
+    C, R = od.gather_rows(pg, 1)
+    np.testing.assert_array_equal(C, [[10, 11], [13, 14]])
+    np.testing.assert_array_equal(R, [[12], [15]])
+    # split fp8: E4M3 codes 0x38 = 1.0, 0x40 = 2.0, 0x30 = 0.5, 0xB8 = -1.0, times the token's scale
+    lat = np.array([[[0x38, 0x40], [0x30, 0xB8], [0x7F, 0x7F]]], dtype=np.uint8)
+    scale = np.array([[2.0, 0.25, nan]], dtype=np.float32)
+    rope = _bf16_bits([[[3], [-6], [nan]]])
+    f8 = DecodeInputs(wl=_tiny_wl("split", 1, 3, dtype="fp8"), lens=np.array([2], dtype=np.int32),
+                      q_C=z, q_R=z, W_UK=z, W_UV=z, latent=lat, rope=rope, scale=scale)
+    C, R = od.gather_rows(f8, 0)
+    np.testing.assert_array_equal(C, [[2.0, 4.0], [0.125, -0.25]])
+    np.testing.assert_array_equal(R, [[3], [-6]])
+
+
+def test_gather_rows_hand_placed():
+    check_gather_rows_hand_placed()
+
+
+_gather = od.gather_rows
+
+
+def _mut_gather_packed_columns_swapped(inp, b):
+    if inp.wl.layout != "packed":
+        return _gather(inp, b)
+    rows = od.decode_bf16(inp.kv[b, :int(inp.lens[b])])
+    return rows[:, inp.wl.d_R:], rows[:, :inp.wl.d_R]
+
+
+def _mut_gather_paged_index_transposed(inp, b):
+    if inp.wl.layout != "paged":
+        return _gather(inp, b)
+    P, L, d_c = inp.wl.page_size, int(inp.lens[b]), inp.wl.d_c
+    j = np.arange(L)
+    rows = od.decode_bf16(inp.pool[inp.block_table[b, j % P], j // P])
+    return rows[:, :d_c], rows[:, d_c:]
+
+
+def _mut_gather_paged_sequence_order(inp, b):
+    if inp.wl.layout != "paged":
+        return _gather(inp, b)
+    P, L, d_c = inp.wl.page_size, int(inp.lens[b]), inp.wl.d_c
+    j = np.arange(L)
+    rows = od.decode_bf16(inp.pool[inp.block_table.reshape(-1)[j // P], j % P])   # ignores the sequence
+    return rows[:, :d_c], rows[:, d_c:]
+
+
+def _mut_gather_fp8_scale_dropped(inp, b):
+    if inp.wl.dtype != "fp8":
+        return _gather(inp, b)
+    L = int(inp.lens[b])
+    return od.decode_e4m3(inp.latent[b, :L]), od.decode_bf16(inp.rope[b, :L])
+
+
+def _mut_relative_l2_max_norm(x, ref):
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    m = ~np.isnan(ref)
+    den = np.max(np.abs(ref[m])) if m.any() else 0.0
+    num = np.max(np.abs((x - ref)[m])) if m.any() else 0.0
+    return float(num / den) if den else float(num)
+
+
+def _mut_relative_l2_squared(x, ref):
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    m = ~np.isnan(ref)
+    num, den = np.sum((x - ref)[m] ** 2), np.sum(ref[m] ** 2)
+    return float(num / den) if den else float(num)
+
+
+GATHER_MUTANTS = {
+    "packed_columns_swapped": ("gather_rows", _mut_gather_packed_columns_swapped),
+    "paged_page_and_slot_swapped": ("gather_rows", _mut_gather_paged_index_transposed),
+    "paged_ignores_sequence": ("gather_rows", _mut_gather_paged_sequence_order),
+    "fp8_scale_dropped": ("gather_rows", _mut_gather_fp8_scale_dropped),
+    "relative_l2_max_norm": ("relative_l2", _mut_relative_l2_max_norm),
+    "relative_l2_squared": ("relative_l2", _mut_relative_l2_squared),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATHER_MUTANTS))
+def test_planted_gather_and_metric_mistakes_are_caught(name, monkeypatch):
+    attr, fn = GATHER_MUTANTS[name]
+    monkeypatch.setattr(od, attr, fn)
+    failures = 0
+    for chk in (check_gather_rows_hand_placed, check_relative_l2_hand_cases):
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures >= 1, f"planted mistake {name!r} passed every pin"

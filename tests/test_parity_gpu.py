@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) against the CPU oracle, on the GPU.
 
-Tolerance (relative L2 over all compared entries): 1e-5 for the fp32 path, 1e-2 for bf16/fp8,
-against the float64 oracle.  Full-size workloads compare sampled (sequence, head) pairs, which
+Tolerance (relative L2 of each compared (sequence, head) pair on its own): 1e-5 for the fp32
+path, 1e-2 for bf16/fp8, against the float64 oracle.  Full-size workloads compare sampled (sequence, head) pairs, which
 the oracle computes one by one, plus properties that hold at any size.
 """
 from __future__ import annotations
@@ -46,7 +46,29 @@ def run_gpu(inp, num_splits=0):
             "o": o.cpu().numpy().astype(np.float64)}
 
 
+def per_pair_errors(got, ref, mask):
+    """Relative L2 of every compared (sequence, head) pair on its own, per output.
+
+    Returns {key: (max error, (b, h) of the max, global error over all pairs)}.  A pair whose
+    reference row is all zero (an empty sequence's o_lat / o) is checked exactly elsewhere."""
+    out = {}
+    for key in ("q_abs", "o_lat", "o"):
+        worst, where = 0.0, None
+        for b, h in zip(*np.nonzero(mask)):
+            r = ref[key][b, h]
+            if not np.any(r):
+                continue
+            e = oracle.relative_l2(got[key][b, h], r)
+            if not e <= worst:     # NaN errors are the worst of all
+                worst, where = e, (int(b), int(h))
+        out[key] = (worst, where, oracle.relative_l2(got[key][mask], ref[key][mask]))
+    return out
+
+
 def compare(inp, got, ref, pairs=None, tol=None):
+    """Every compared (sequence, head) pair must meet the tolerance on its own: relative L2 of
+    its q_abs, o_lat and o rows against the oracle's.  A global norm would let one head's error
+    hide among the rest (one head 5 % off among 128 moves the global figure by 0.44 %)."""
     tol = TOL[inp.wl.dtype] if tol is None else tol
     B, H = inp.wl.B, inp.wl.H
     mask = np.zeros((B, H), dtype=bool)
@@ -56,19 +78,19 @@ def compare(inp, got, ref, pairs=None, tol=None):
         for b, h in pairs:
             mask[b, h] = True
     nonempty = mask & (inp.lens[:, None] > 0)
-    errs = {}
-    for key in ("q_abs", "o_lat", "o"):
-        g, r = got[key][mask], ref[key][mask]
-        errs[key] = oracle.relative_l2(g, r)
+    per = per_pair_errors(got, ref, mask)
+    errs = {k: v[2] for k, v in per.items()}
+    errs.update({f"{k}_max_pair": v[0] for k, v in per.items()})
     if nonempty.any():
         errs["lse_abs"] = float(np.max(np.abs(got["lse"][nonempty] - ref["lse"][nonempty])))
     empty = mask & (inp.lens[:, None] == 0)
     if empty.any():
         assert np.all(got["o_lat"][empty] == 0.0) and np.all(got["o"][empty] == 0.0)
         assert np.all(np.isneginf(got["lse"][empty]))
-    print(f"[parity] {inp.wl.name}: {errs}", flush=True)
+    worst = {k: v[1] for k, v in per.items()}
+    print(f"[parity] {inp.wl.name}: {errs} worst pairs {worst}", flush=True)
     for key in ("q_abs", "o_lat", "o"):
-        assert errs[key] <= tol, (key, errs[key])
+        assert per[key][0] <= tol, (key, "pair", per[key][1], per[key][0])
     if "lse_abs" in errs:
         assert errs["lse_abs"] <= (1e-4 if inp.wl.dtype == "f32" else 2e-2), errs
     return errs
@@ -248,10 +270,14 @@ def test_projections_batch_sweep(B):
     o_lat = torch.from_numpy(ref["o_lat"].astype(np.float32)).to("cuda")
     o = ops.mla_uv_out(o_lat, dev["W_UV"])
     torch.cuda.synchronize()
-    e_q = oracle.relative_l2(q_abs.float().cpu().numpy().astype(np.float64), ref["q_abs"])
-    e_o = oracle.relative_l2(o.cpu().numpy().astype(np.float64), ref["o"])
-    print(f"[parity] projections B={B}: q_abs {e_q:.3e} o {e_o:.3e}", flush=True)
-    # q_abs is rounded once to bf16 (2^-9 relative); o is an fp32 product of exact inputs
+    got = {"q_abs": q_abs.float().cpu().numpy().astype(np.float64), "o_lat": ref["o_lat"],
+           "o": o.cpu().numpy().astype(np.float64)}
+    per = per_pair_errors(got, ref, np.ones((B, wl.H), dtype=bool))
+    e_q, e_o = per["q_abs"][0], per["o"][0]
+    print(f"[parity] projections B={B}: worst pair q_abs {e_q:.3e} {per['q_abs'][1]} o {e_o:.3e} {per['o'][1]}",
+          flush=True)
+    # per (sequence, head): q_abs is rounded once to bf16 (2^-9 relative); o is an fp32 product of
+    # exact inputs
     assert e_q <= 4e-3 and e_o <= 1e-4
 
 
