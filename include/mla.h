@@ -33,10 +33,11 @@
  *    page id outside the pool, is undefined behaviour.
  *  - Results are bitwise reproducible for fixed arguments: every sum is taken in a fixed order.
  *    Some kernels exchange data between workgroups of one launch (mla_decode_combine_uv at
- *    small batch): the producers write with device-coherent (agent-scope) stores, wait until
+ *    small batch, mla_decode_step's one-launch form): the producers write with device-coherent (agent-scope) stores, wait until
  *    those stores have completed (s_waitcnt vmcnt(0)), then raise an agent-scope counter with
- *    an integer atomic add; a consumer reads the data with device-coherent loads only after it
- *    has seen the counter's final value, and adds the parts in a fixed order, so the result does
+ *    an integer atomic add (mla_decode_step: set one flag word per consumer); a consumer reads
+ *    the data with device-coherent loads only after it has seen the counter's final value (its
+ *    flags), and adds the parts in a fixed order, so the result does
  *    not depend on which workgroup finished last.  No floating-point atomics are used.
  *  - Calls on different streams are independent; the library keeps no state
  *    other than the per-thread last HIP error.
@@ -232,6 +233,40 @@ int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, in
  */
 int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out, int B, int H, int d_h,
                int d_c, void* stream);
+
+/*
+ * mla_decode_step -- the whole absorbed decode step in one call: mla_absorb_q, mla_decode_attn and
+ * mla_uv_out of the same arguments ("Grouped-query and latent attention", sections "The
+ * absorption trick" and "Why a separate rotary key"):
+ *   out[b,h] = W_UV[h] sum_j a[b,h,j] c[b,j],  a = softmax_j scale (q'[b,h] . c[b,j] + q_R[b,h] . k_R[b,j]),
+ *   q'[b,h]  = W_UK[h]^T q_C[b,h]
+ *   q_C [B,H,d_h], q_R [B,H,d_R], W_UK and W_UV [H,d_h,d_c], all in `dtype` (MLA_F32 or MLA_BF16);
+ *   cache, seq_lens, max_len, scale: as for mla_decode_attn
+ *   out      [B,H,d_h] float32 (written)
+ *   q_abs    [B,H,d_c] in `dtype`, o_latent [B,H,d_c] float32, lse [B,H] float32: written when not
+ *            NULL (the intermediate results of the three calls; NULL = not needed)
+ *   workspace at least mla_decode_step_workspace_bytes(B, H, d_c, max_len) bytes, 16-byte aligned.
+ *            Its first mla-defined bytes are a flag region that must be ZERO before the first call
+ *            (zero-filled memory, or mla_decode_step_init); every call leaves it zero.  The int32
+ *            at byte 0 is a sticky error word: nonzero after a one-launch call in which a wait
+ *            between workgroups gave up (after 20 ms; results of that call are invalid, and the
+ *            workspace must be re-initialised with mla_decode_step_init).
+ * One launch when: dtype and both cache parts MLA_BF16, B == 1, H == 128, d_h == 128, d_c == 512,
+ * d_R == 64, max_len <= 4096, paged page_size a multiple of 32, 16-byte aligned inputs, cache rows
+ * and o_latent, 4-byte aligned q_abs, and at least 256 compute units on the current device.  That
+ * kernel keeps one workgroup on each of 256 compute units, and its workgroups wait for each other:
+ * do not run it concurrently with other work that occupies compute units for a long time (a wait
+ * that cannot complete gives up after 20 ms and sets the error word).  Otherwise the step is the
+ * three calls, mla_absorb_q -> mla_decode_partial_warm (W_UV warmed) -> mla_decode_combine_uv,
+ * with the automatic split count, their buffers carved from the workspace.
+ * Errors as for those calls; nothing is launched when validation fails.  B == 0 is a no-op.
+ */
+size_t mla_decode_step_workspace_bytes(int B, int H, int d_c, int max_len);
+int mla_decode_step_init(void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_step(const void* q_C, const void* q_R, const void* W_UK, const void* W_UV, int dtype,
+                    const mla_cache_desc* cache, const int32_t* seq_lens, int max_len, int B, int H, int d_h,
+                    int d_c, int d_R, float scale, void* workspace, size_t workspace_bytes, void* q_abs,
+                    float* o_latent, float* lse, float* out, void* stream);
 
 /*
  * Workspace (device bytes) mla_cache_append needs: (D / 512) x B x 576 float32 partial sums of

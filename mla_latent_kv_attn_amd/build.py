@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_amd.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_abi.hip", "decode_generic.hip", "absorb_uv_mfma.hip", "decode_partial_mfma.hip",
+SOURCES = ["mla_abi.hip", "decode_generic.hip", "absorb_uv_mfma.hip", "decode_partial_mfma.hip", "decode_step.hip",
            "decode_partial_small.hip", "cache_append.hip",
            "mha_decode.hip", "proj.hip"]
 
@@ -52,7 +52,7 @@ def hipcc() -> str:
 # Kernels whose DMA pipeline counts outstanding vector-memory operations (s_waitcnt vmcnt): a
 # spill to scratch memory inside them would add scratch loads/stores to that count, so they must
 # use no scratch (SGPR spills into VGPR lanes are fine).
-NO_SCRATCH_KERNELS = ("k_partial_mfma", "k_partial_small")
+NO_SCRATCH_KERNELS = ("k_partial_mfma", "k_partial_small", "k_step_b1")
 
 
 def _check_spills(src: str, remarks: str) -> None:

@@ -1,0 +1,505 @@
+// The whole absorbed decode step for one sequence in one launch (bf16, DeepSeek-V3 shape:
+// H = 128, d_h = 128, d_c = 512, d_R = 64, at most 4096 cached tokens):
+//
+//   q'[h]    = W_UK[h]^T q_C[h]                                  (phase A, "the absorption trick")
+//   s_j      = scale (q'[h] . c_j + q_R[h] . k_R,j),  a = softmax_j s   (phase B)
+//   o_lat[h] = sum_j a_j c_j,   o[h] = W_UV[h] o_lat[h]          (phase B partials, phase C)
+//
+// ("Grouped-query and latent attention", sections "The absorption trick" and "Why a separate
+// rotary key".)  At one sequence the step moves 33.5 MB of weights and 4.7 MB of cache, and each
+// of the three separate passes is too short to get the memory system up to speed: a cold 16.8 MB
+// stream over the whole chip takes about 6 us.  Here every load of the step is issued at kernel
+// entry, W_UK first, so the W_UK, cache and W_UV streams overlap, and the dependencies between
+// the phases are handed over inside the launch.
+//
+// Grid: 256 workgroups (one per CU; the LDS use forces that), 512 threads.  Waves 0-3 compute;
+// waves 4-7 only move data into LDS and then take part in the workgroup's barriers, so no compute
+// wave ever waits for a prefetch it did not need (s_waitcnt counts a wave's own memory operations
+// in order).  Workgroup r sits on XCD r % 8; slot r / 8:
+//  * slots 0-15: attention workgroup (split s = 4 (r % 8) + slot / 4 of the token tiles, head
+//    block g = slot % 4 of 32 heads); the four head blocks of a split share an XCD, so a tile is
+//    read from HBM once and from that XCD's L2 three times;
+//  * slots 16-31: projection workgroup for head h = 16 (r % 8) + slot - 16.
+// Phase A (every workgroup, compute wave w): the 16 KB piece of W_UK for head 32 w + r / 8 and
+// latent columns 64 (r % 8) .. + 63; the 64 sums are rounded to bf16 and published.
+// Phase B (attention): the split's (at most four) 32-token tiles were DMA'd into LDS by the loader
+// waves, one 9 KB column slice per compute wave.  Wave w computes the partial scores of its
+// latent columns 128 w .. + 127 and rope dimensions 16 w .. + 15 (9 MFMA 32x32x16 per tile), the
+// four partials are added through LDS, the softmax of the split is exact (all of its scores are
+// held at once: its maximum, then 2^(s - m)), and wave w multiplies its columns by the
+// probabilities (8 MFMA per tile).  The partial (m, l, acc) per head is published.
+// Phase C (projection): W_UV[h] (128 KB) was DMA'd into LDS at entry; the 32 splits' partials of
+// head h are merged (log-sum-exp) into o_lat[h] and multiplied by W_UV[h].
+//
+// Hand-over between workgroups: the producer writes its data with device-coherent stores (sc1),
+// waits for them to complete (s_waitcnt vmcnt(0)), then sets one flag word per consumer (sc1
+// store).  Each consumer polls only its own flag words (one vector load per poll), resets them
+// after it has seen them all, and then reads the data with device-coherent loads.  There is no
+// counter that many workgroups update or poll: measured on the box, 128 workgroups polling one
+// counter saw it change about 5 us late.  Every wait gives up after 20 ms of wall-clock time
+// (s_memrealtime) and records an error word, so every wave always reaches the end.  The flags
+// must be zero before the first launch; every launch leaves them zero.
+#include "partial_common.h"
+#include "step_internal.h"
+
+namespace mla {
+
+namespace {
+constexpr int kSSlice = 9216;                  // LDS bytes per tile and wave slice (latent 8 KB + rope 1 KB)
+constexpr int kSRope = 8192;
+constexpr int kRingBytes = kStepTiles * 4 * kSSlice;   // 147456
+constexpr int kXBytes = 16384;                 // exchange buffer
+constexpr int kLdsBytes = kRingBytes + kXBytes;        // 163840: the whole LDS of a CU
+constexpr int kPRow = 272;                     // bytes per head row of the probabilities (128 tokens + pad)
+constexpr unsigned kCoh = 16;                  // buffer cache policy: sc1 (device-coherent)
+constexpr uint64_t kWaitTicks = 2000000;       // 20 ms at the 100 MHz s_memrealtime clock
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void coh_store4(const __amdgpu_buffer_rsrc_t& r, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCoh);
+}
+__device__ __forceinline__ u32x4 coh_load4(const __amdgpu_buffer_rsrc_t& r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoh);
+}
+__device__ __forceinline__ u32x2 coh_load2(const __amdgpu_buffer_rsrc_t& r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCoh);
+}
+__device__ __forceinline__ void coh_store_i32(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Waits until the flag word of every active lane (lane < n) is nonzero, then clears them.
+// Uniform; gives up after kWaitTicks and records the error.
+__device__ __forceinline__ void wait_flags(int* flags, int lane, int n, int* err) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  int* p = flags + (lane < n ? lane : 0);
+  while (true) {
+    const int v = lane < n ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+    if (__builtin_amdgcn_ballot_w64(v == 0) == 0) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      if (lane == 0) coh_store_i32(err, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane < n) coh_store_i32(p, 0);
+  compiler_fence();
+}
+
+// Sum of 8 per-lane values over lane bits 5, 4, 3 (d = 32, 16, 8) by halving exchange; afterwards
+// lane l holds the sum of value index (l >> 3) & 7.  (The pair passes through an empty asm so
+// that the compiler keeps the selects as register selects.)
+__device__ __forceinline__ float sum8_over_bits543(float (&v)[8], int lane) {
+#pragma unroll
+  for (int step = 0; step < 3; ++step) {
+    const int d = 32 >> step;
+    const int half = 4 >> step;
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      float lo = v[i], hi = v[i + half];
+      asm("" : "+v"(lo), "+v"(hi));
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
+      v[i] = keep + __shfl_xor(send, d, 64);
+    }
+  }
+  return v[0];
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+}  // namespace
+
+__global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = r >> 3, xcd = r & 7;
+  const bool attn = slot < 16;
+  const int split = 4 * xcd + (slot >> 2);
+  const int g = slot & 3;
+  const int hproj = 16 * xcd + slot - 16;
+  uint8_t* xb = lds + kRingBytes;
+
+  // tile range of this split (attention): T tiles of the sequence cut evenly over kStepSplits
+  auto tile_range = [&](int len, int& t0, int& ntl) __attribute__((always_inline)) {
+    const int T = min(tiles_of(len), kStepSplits * kStepTiles);
+    t0 = split * T / kStepSplits;
+    ntl = (split + 1) * T / kStepSplits - t0;
+  };
+
+  // ------------------------------------------------------------------ loader waves
+  if (wave >= 4) {
+    const int lw = wave - 4;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (attn) {
+      const int len = max(load_uniform_i32(a.seq_lens), 0);
+      int t0, ntl;
+      tile_range(len, t0, ntl);
+      const uint32_t lstride = (uint32_t)a.lat_st * 2u;
+      for (int i = 0; i < ntl; ++i) {
+        const int tok0 = (t0 + i) * kTile;
+        const int last = __builtin_amdgcn_readfirstlane(min(kTile, len - tok0) - 1);
+        int64_t lrow0, rrow0;
+        int tslot0;
+        if (a.block_table) {
+          const int page = load_uniform_i32(a.block_table + tok0 / a.page_size);
+          lrow0 = (int64_t)page * a.lat_sb;
+          rrow0 = (int64_t)page * a.rope_sb;
+          tslot0 = tok0 % a.page_size;
+        } else {
+          lrow0 = 0;
+          rrow0 = 0;
+          tslot0 = tok0;
+        }
+        const uint8_t* lbase = (const uint8_t*)uniform_ptr((const uint8_t*)a.latent +
+                                                           (lrow0 + (int64_t)tslot0 * a.lat_st) * 2 + 256 * lw);
+        const uint8_t* rbase = (const uint8_t*)uniform_ptr((const uint8_t*)a.rope +
+                                                           (rrow0 + (int64_t)tslot0 * a.rope_st) * 2 + 32 * lw);
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(lds + (i * 4 + lw) * kSSlice));
+        // latent row q of the slice: 256 bytes, 16-byte chunk c at position c ^ (q & 15); rows past
+        // the sequence's end are loaded from its last row (finite data, masked later)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int q = 4 * k + (ln >> 4);
+          const uint32_t voff = (uint32_t)min(q, last) * lstride + 16u * (uint32_t)((ln & 15) ^ (q & 15));
+          lds_dma16(lbase, voff, st + 1024 * k);
+        }
+        // rope row q: 32 bytes, chunk c at position c ^ ((q >> 3) & 1)
+        const int rq = ln >> 1;
+        const uint32_t roff =
+            (uint32_t)(min(rq, last) * (int)a.rope_st * 2) + 16u * (uint32_t)((ln & 1) ^ ((rq >> 3) & 1));
+        lds_dma16(rbase, roff, st + kSRope);
+      }
+    } else {
+      // W_UV[h]: row i (1 KB) at LDS i * 1024, 16-byte chunk c at position c ^ (i & 63)
+      const uint8_t* wbase = (const uint8_t*)a.W_UV + (int64_t)hproj * 128 * 1024;
+      for (int k = 0; k < 32; ++k) {
+        const int i = 32 * lw + k;
+        lds_dma16(wbase + i * 1024, 16u * (uint32_t)(ln ^ (i & 63)),
+                  __builtin_amdgcn_readfirstlane(lds_addr(lds + i * 1024)));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();   // B1: the prefetched data is in LDS
+    // then the barriers the compute waves take after B1 (attention: two per tile, the
+    // probabilities, the published partials; projection: three), so that every barrier of the
+    // workgroup sees all eight waves
+    int nb = 3;
+    if (attn) {
+      int t0, ntl;
+      tile_range(max(load_uniform_i32(a.seq_lens), 0), t0, ntl);
+      nb = 2 + 2 * ntl;
+    }
+    for (int k = 0; k < nb; ++k) lds_barrier();
+    return;
+  }
+
+  // ------------------------------------------------------------------ phase A: absorb piece
+  // compute wave w: q'[hw][c0 .. c0 + 63], hw = 32 w + r / 8, c0 = 64 (r % 8); lane (rg, cc) sums
+  // rows 16 rg .. 16 rg + 15 of columns c0 + 8 cc .. + 7
+  {
+    const int hw = 32 * wave + (r >> 3);
+    const int c0 = (r & 7) * 64;
+    const int rg = lane >> 3, cc = lane & 7;
+    u32x4 qv = {0u, 0u, 0u, 0u};
+    if (lane < 16) qv = *(const u32x4*)(a.q_C + hw * 128 + lane * 8);
+    u32x4 wv[16];
+    const uint16_t* wp = a.W_UK + ((int64_t)hw * 128 + 16 * rg) * 512 + c0 + cc * 8;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) wv[k] = *(const u32x4*)(wp + k * 512);
+    uint8_t* xq = xb + wave * 256;
+    if (lane < 16) *(u32x4*)(xq + lane * 16) = qv;
+    const u32x4 qa = *(const u32x4*)(xq + 32 * rg), qb = *(const u32x4*)(xq + 32 * rg + 16);
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t qw = k < 8 ? qa[(k & 7) >> 1] : qb[(k & 7) >> 1];
+      const float q = (k & 1) ? bf16_hi(qw) : bf16_lo(qw);
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        acc[2 * c2] = fmaf(q, bf16_lo(wv[k][c2]), acc[2 * c2]);
+        acc[2 * c2 + 1] = fmaf(q, bf16_hi(wv[k][c2]), acc[2 * c2 + 1]);
+      }
+    }
+    // lane (rg, cc) now holds column c0 + 8 cc + rg; lanes with rg even store two columns
+    const float s = sum8_over_bits543(acc, lane);
+    const float s1 = __shfl_xor(s, 8, 64);
+    if ((rg & 1) == 0)
+      __hip_atomic_store((uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg), pack_bf16x2(s, s1), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    // one flag per consumer: compute wave cw = (r % 8) / 2 of each attention workgroup of head
+    // block `wave`, producer index 2 (r / 8) + r % 2 among its 64 producers
+    if (lane < kStepSplits) {
+      const int cw = (r & 7) >> 1, p = 2 * (r >> 3) + (r & 1);
+      coh_store_i32(a.fa + ((wave * kStepSplits + lane) * 4 + cw) * 64 + p, 1);
+    }
+  }
+
+  const int len = max(load_uniform_i32(a.seq_lens), 0);
+  if (attn) {
+    // ---------------------------------------------------------------- phase B: attention
+    const int cw = wave;
+    const int hl = lane & 31, hf = lane >> 5;
+    int t0, ntl;
+    tile_range(len, t0, ntl);
+    // this wave's folded-query slice: latent k-steps 8 cw .. 8 cw + 7 (qf[0..7]) and rope k-step cw
+    wait_flags(a.fa + ((g * kStepSplits + split) * 4 + cw) * 64, lane, 64, a.err);
+    const __amdgpu_buffer_rsrc_t qr = rsrc(a.qp);
+    u32x4 qf[9];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[j] = coh_load4(qr, (uint32_t)(((32 * g + hl) * 512 + 128 * cw + 16 * j + 8 * hf) * 2));
+    qf[8] = *(const u32x4*)(a.q_R + (32 * g + hl) * 64 + 16 * cw + 8 * hf);
+    lds_barrier();   // B1: tiles landed
+
+    // scores: S[i] = partial S^T of tile i (32 tokens x 32 heads) over this wave's columns.  The
+    // rows of a tile are read in a permuted order (bits 2 and 3 swapped) so that the softmax
+    // layout below sees four consecutive tokens per lane.
+    const int srow = pi_row(hl);
+    const int sc_row = srow * 256, sc_x = srow & 15;
+    const int rope_rd = kSRope + srow * 32 + 16 * (hf ^ ((srow >> 3) & 1));
+    f32x16 S[kStepTiles];
+#pragma unroll
+    for (int i = 0; i < kStepTiles; ++i) {
+      S[i] = f32x16{};
+      if (i < ntl) {
+        const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+        u32x4 av[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] = *(const u32x4*)(st + sc_row + 16 * ((2 * j + hf) ^ sc_x));
+        const u32x4 rv = *(const u32x4*)(st + rope_rd);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S[i] = mfma32x32x16(av[j], qf[j], S[i]);
+        S[i] = mfma32x32x16(rv, qf[8], S[i]);
+      }
+    }
+    // add the four waves' partials, one tile per round: wave w writes its block head-major (128 B
+    // per head, chunk c of head n at position c ^ ((n >> 1) & 7)); then wave w reads heads
+    // 8 w .. 8 w + 7, chunk sc (4 consecutive tokens) per lane
+    const int sn = 8 * cw + (lane >> 3), sc = lane & 7;
+    const int tok_c = 4 * ((sc >> 1) & 1) + 8 * (sc & 1) + 16 * (sc >> 2);
+    f32x4 sv[kStepTiles];
+#pragma unroll
+    for (int i = 0; i < kStepTiles; ++i) {
+      sv[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (i < ntl) {
+        uint8_t* sb = xb + cw * 4096 + hl * 128;
+        const int xs = (hl >> 1) & 7;
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          *(f32x4*)(sb + 16 * ((2 * v4 + hf) ^ xs)) =
+              f32x4{S[i][4 * v4], S[i][4 * v4 + 1], S[i][4 * v4 + 2], S[i][4 * v4 + 3]};
+        lds_barrier();
+        const uint8_t* rb = xb + sn * 128 + 16 * (sc ^ ((sn >> 1) & 7));
+        f32x4 x = *(const f32x4*)rb;
+#pragma unroll
+        for (int q = 1; q < 4; ++q) x += *(const f32x4*)(rb + 4096 * q);
+        const int tok = (t0 + i) * kTile + tok_c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[i][e] = tok + e < len ? x[e] * a.sl2 : -INFINITY;
+        lds_barrier();
+      }
+    }
+    // exact softmax over the split (base 2, scale folded in): max, probabilities, sum
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kStepTiles; ++i)
+      m = fmaxf(m, fmaxf(fmaxf(sv[i][0], sv[i][1]), fmaxf(sv[i][2], sv[i][3])));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < kStepTiles; ++i) {
+      if (i < ntl) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(sv[i][e] - m);
+        l += (p[0] + p[1]) + (p[2] + p[3]);
+        *(u32x2*)(xb + sn * kPRow + 2 * (kTile * i + tok_c)) = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      }
+    }
+    l += __shfl_xor(l, 1, 64);
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    if (sc == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m), __float_as_uint(l)}, rsrc(a.part_ml),
+                                            (int)((split * 128 + 32 * g + sn) * 8), 0, kCoh);
+    lds_barrier();   // the probabilities of all 32 heads are in LDS
+
+    // value: acc[cb] = O^T block (latent columns 128 cw + 32 cb .. + 31) x (32 heads)
+    if (ntl > 0) {
+      const int G = lane >> 4;
+      const int vrow0 = 8 * (G >> 1) + ((lane & 15) >> 2);
+      f32x16 acc[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < kStepTiles; ++i) {
+        if (i < ntl) {
+          const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 pv = *(const u32x4*)(xb + hl * kPRow + 2 * (kTile * i + 16 * ks + 8 * hf));
+            const int R = 16 * ks + vrow0;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              const int cch = 4 * cb + 2 * (G & 1) + ((lane & 3) >> 1);
+              const uint8_t* pa = st + R * 256 + 16 * (cch ^ (R & 15)) + 8 * (lane & 1);
+              const uint8_t* pb = st + (R + 4) * 256 + 16 * (cch ^ ((R + 4) & 15)) + 8 * (lane & 1);
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pb));
+              const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+              acc[cb] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pv, acc[cb]);
+            }
+          }
+        }
+      }
+      // partial rows to the workspace: each 32 x 32 block is turned into head rows through this
+      // wave's own ring slices (no other wave reads them), then stored as whole 128-byte lines
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int trow = ln >> 3, tch = ln & 7;
+      const int xs = ((ln & 31) >> 1) & 7;
+      const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        uint8_t* tb = lds + ((cb >> 1) * 4 + cw) * kSSlice + (cb & 1) * 4096;
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          *(f32x4*)(tb + (ln & 31) * 128 + 16 * ((2 * v4 + (ln >> 5)) ^ xs)) =
+              f32x4{acc[cb][4 * v4], acc[cb][4 * v4 + 1], acc[cb][4 * v4 + 2], acc[cb][4 * v4 + 3]};
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint8_t* tb = lds + ((cb >> 1) * 4 + cw) * kSSlice + (cb & 1) * 4096;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 8 * q + trow;
+          const u32x4 v = *(const u32x4*)(tb + row * 128 + 16 * (tch ^ ((row >> 1) & 7)));
+          coh_store4(pr, (uint32_t)(((split * 128 + 32 * g + row) * 512 + 128 * cw + 32 * cb + 4 * tch) * 4), v);
+        }
+      }
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    lds_barrier();   // every wave's partial stores have completed
+    if (cw == 0 && lane < 32) coh_store_i32(a.fb + (32 * g + lane) * kStepSplits + split, 1);
+    return;
+  }
+
+  // ------------------------------------------------------------------ phase C: merge + W_UV
+  const int h = hproj;
+  if (wave == 0) wait_flags(a.fb + h * kStepSplits, lane, kStepSplits, a.err);
+  lds_barrier();   // B1: W_UV[h] in LDS, every split of head h published
+  float* ws = (float*)(xb + 1024);        // [32] split weights
+  float* ol = (float*)(xb + 2048);        // [512] o_lat[h]
+  float* half1 = (float*)(xb + 4096);     // [128] float4: the second half's sums
+  float* stat = (float*)(xb + 8192);      // M, L
+  if (wave == 0) {
+    // (m, l) of the splits: lane s < 32
+    u32x2 ml = {0u, 0u};
+    if (lane < kStepSplits) ml = coh_load2(rsrc(a.part_ml), (uint32_t)((lane * 128 + h) * 8));
+    const float ms = lane < kStepSplits ? __uint_as_float(ml[0]) : -INFINITY;
+    const float ls = lane < kStepSplits ? __uint_as_float(ml[1]) : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    const float w = (ms == -INFINITY || M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    float L = w * ls;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d, 64);
+    if (lane < kStepSplits) ws[lane] = w;
+    if (lane == 0) {
+      stat[0] = M;
+      stat[1] = L;
+    }
+  }
+  lds_barrier();
+  {
+    // thread t: columns 4 (t % 128) .. + 3 over splits t / 128 + 2 u
+    const int c4 = tid & 127, hs = tid >> 7;
+    const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+    u32x4 x[kStepSplits / 2];
+#pragma unroll
+    for (int u = 0; u < kStepSplits / 2; ++u)
+      x[u] = coh_load4(pr, (uint32_t)((((hs + 2 * u) * 128 + h) * 512 + 4 * c4) * 4));
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kStepSplits / 2; ++u) {
+      const float w = ws[hs + 2 * u];
+      const f32x4 xv = __builtin_bit_cast(f32x4, x[u]);
+      // a split without tokens has weight 0 and never wrote its rows: select, do not multiply
+      if (w != 0.f) o += w * xv;
+    }
+    if (hs == 1) *(f32x4*)(half1 + 4 * c4) = o;
+    lds_barrier();
+    if (hs == 0) {
+      o += *(const f32x4*)(half1 + 4 * c4);
+      const float M = stat[0], L = stat[1];
+      const float inv = M == -INFINITY ? 0.f : 1.f / L;
+      o *= inv;
+      *(f32x4*)(ol + 4 * c4) = o;
+      if (a.o_latent) *(f32x4*)(a.o_latent + h * 512 + 4 * c4) = o;
+      if (a.lse && tid == 0) a.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * 0.69314718055994530942f;
+    }
+    lds_barrier();
+  }
+  {
+    // out[h][i] = sum_k W_UV[h][i][k] o_lat[k]: thread t takes row i = t / 2, columns
+    // 256 (t % 2) .. + 255 (32 chunks of 8), W from LDS (chunk c of row i at c ^ (i & 63))
+    const int i = tid >> 1, kh = tid & 1;
+    const uint8_t* wr = lds + i * 1024;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < 32; ++q) {
+      const int c = 32 * kh + q;
+      const u32x4 wv = *(const u32x4*)(wr + 16 * (c ^ (i & 63)));
+      const f32x4 xa = *(const f32x4*)(ol + 8 * c), xc = *(const f32x4*)(ol + 8 * c + 4);
+      s0 = fmaf(bf16_lo(wv[0]), xa[0], s0);
+      s1 = fmaf(bf16_hi(wv[0]), xa[1], s1);
+      s0 = fmaf(bf16_lo(wv[1]), xa[2], s0);
+      s1 = fmaf(bf16_hi(wv[1]), xa[3], s1);
+      s0 = fmaf(bf16_lo(wv[2]), xc[0], s0);
+      s1 = fmaf(bf16_hi(wv[2]), xc[1], s1);
+      s0 = fmaf(bf16_lo(wv[3]), xc[2], s0);
+      s1 = fmaf(bf16_hi(wv[3]), xc[3], s1);
+    }
+    float t = s0 + s1;
+    t += __shfl_xor(t, 1, 64);
+    if (kh == 0) a.out[h * 128 + i] = t;
+  }
+}
+
+// Zeroes the flag words (and the error word) of a step workspace: a plain fill kernel, so that it
+// can be captured in a graph.
+__global__ void k_step_zero(int* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_step_b1(const StepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_step_b1, dim3(kStepWGs), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_zero(int* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_step_zero, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace mla

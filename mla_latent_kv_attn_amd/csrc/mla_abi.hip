@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "rows_internal.h"
+#include "step_internal.h"
 
 namespace {
 
@@ -314,6 +315,138 @@ int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, in
   st = hip_status(mla::launch_combine(ca, (hipStream_t)stream));
   if (st != MLA_OK) return st;
   return mla_uv_out(o_latent, W_UV, w_dtype, out, B, H, d_h, d_c, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// The whole decode step behind one call: the one-launch form for one bf16 sequence at the V3 head
+// sizes, otherwise mla_absorb_q -> mla_decode_partial_warm -> mla_decode_combine_uv.
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];   // compute units per device, 0 = not queried yet
+
+int current_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int c = __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&g_cu_count[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// data region of the multi-kernel form: q_abs (up to 4-byte elements), o_latent, decode workspace
+size_t step_multi_data_bytes(int B, int H, int d_c, int max_len) {
+  return round256((size_t)B * H * d_c * 4) + round256((size_t)B * H * d_c * 4) +
+         mla_decode_workspace_bytes(B, H, d_c, max_len, 0);
+}
+size_t step_one_data_bytes() {
+  return round256(mla::kStepQpBytes) + round256(mla::kStepMlBytes) + round256(mla::kStepAccBytes);
+}
+
+bool step_one_launch_fits(int dtype, const mla_cache_desc* c, int max_len, int B, int H, int d_h, int d_c, int d_R,
+                          const void* q_C, const void* q_R, const void* W_UK, const void* W_UV, const void* q_abs,
+                          const float* o_latent) {
+  if (dtype != MLA_BF16 || c->latent_dtype != MLA_BF16 || c->rope_dtype != MLA_BF16) return false;
+  if (B != 1 || H != 128 || d_h != 128 || d_c != 512 || d_R != 64) return false;
+  if (max_len > mla::kStepSplits * mla::kStepTiles * mla::kTile) return false;
+  if (c->block_table && (c->page_size % mla::kTile) != 0) return false;
+  if (!aligned16(q_C) || !aligned16(q_R) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(c->latent) ||
+      !aligned16(c->rope) || ((c->latent_stride_tok * 2) % 16) != 0 || ((c->latent_stride_b * 2) % 16) != 0 ||
+      ((c->rope_stride_tok * 2) % 16) != 0 || ((c->rope_stride_b * 2) % 16) != 0)
+    return false;
+  if ((q_abs && ((uintptr_t)q_abs & 3u) != 0) || (o_latent && !aligned16(o_latent))) return false;
+  return current_device_cus() >= mla::kStepWGs;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_step_workspace_bytes(int B, int H, int d_c, int max_len) {
+  if (B < 1 || H < 1 || d_c < 1 || max_len < 0) return 0;
+  size_t data = step_multi_data_bytes(B, H, d_c, max_len);
+  if (B == 1 && H == 128 && d_c == 512) data = std::max(data, step_one_data_bytes());
+  return mla::kStepFlagBytes + data;
+}
+
+int mla_decode_step_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla::kStepFlagBytes) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  return hip_status(mla::launch_step_zero((int*)workspace, (int64_t)(mla::kStepFlagBytes / 4), (hipStream_t)stream));
+}
+
+int mla_decode_step(const void* q_C, const void* q_R, const void* W_UK, const void* W_UV, int dtype,
+                    const mla_cache_desc* cache, const int32_t* seq_lens, int max_len, int B, int H, int d_h,
+                    int d_c, int d_R, float scale, void* workspace, size_t workspace_bytes, void* q_abs,
+                    float* o_latent, float* lse, float* out, void* stream) {
+  if (B < 0 || H < 1 || d_h < 1 || d_c < 4 || d_R < 1 || max_len < 0) return MLA_ERR_SHAPE;
+  if (B > mla::kMaxB) return MLA_ERR_UNSUPPORTED;
+  if (!known_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!cache) return MLA_ERR_NULL;
+  if (!known_dtype(cache->latent_dtype) || !known_dtype(cache->rope_dtype)) return MLA_ERR_DTYPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q_C || !q_R || !W_UK || !W_UV || !seq_lens || !out || !cache->latent || !cache->rope) return MLA_ERR_NULL;
+  if (cache->latent_stride_tok < 1 || cache->rope_stride_tok < 1 || cache->latent_stride_b < 0 ||
+      cache->rope_stride_b < 0)
+    return MLA_ERR_SHAPE;
+  if (cache->block_table && (cache->page_size < 1 || cache->max_pages < 1 ||
+                             (int64_t)cache->max_pages * cache->page_size < (int64_t)max_len))
+    return MLA_ERR_SHAPE;
+  const size_t need = mla_decode_step_workspace_bytes(B, H, d_c, max_len);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  char* data = ws + mla::kStepFlagBytes;
+  if (step_one_launch_fits(dtype, cache, max_len, B, H, d_h, d_c, d_R, q_C, q_R, W_UK, W_UV, q_abs, o_latent)) {
+    mla::StepArgs a;
+    a.q_C = (const uint16_t*)q_C;
+    a.q_R = (const uint16_t*)q_R;
+    a.W_UK = (const uint16_t*)W_UK;
+    a.W_UV = (const uint16_t*)W_UV;
+    a.latent = cache->latent;
+    a.rope = cache->rope;
+    a.block_table = cache->block_table;
+    a.lat_sb = cache->latent_stride_b;
+    a.lat_st = cache->latent_stride_tok;
+    a.rope_sb = cache->rope_stride_b;
+    a.rope_st = cache->rope_stride_tok;
+    a.page_size = cache->block_table ? cache->page_size : 1;
+    a.seq_lens = seq_lens;
+    a.sl2 = scale * 1.4426950408889634f;
+    a.err = (int*)ws;
+    a.fa = (int*)(ws + mla::kStepErrBytes);
+    a.fb = a.fa + mla::kStepFaInts;
+    a.qp = q_abs ? (uint16_t*)q_abs : (uint16_t*)data;
+    a.part_ml = (float*)(data + round256(mla::kStepQpBytes));
+    a.part_acc = (float*)(data + round256(mla::kStepQpBytes) + round256(mla::kStepMlBytes));
+    a.out = out;
+    a.o_latent = o_latent;
+    a.lse = lse;
+    return hip_status(mla::launch_step_b1(a, s));
+  }
+  // multi-kernel form
+  const int qe = dtype == MLA_F32 ? 4 : 2;
+  void* qa = q_abs ? q_abs : (void*)data;
+  float* ol = o_latent ? o_latent : (float*)(data + round256((size_t)B * H * d_c * 4));
+  char* dws = data + 2 * round256((size_t)B * H * d_c * 4);
+  const size_t dws_bytes = mla_decode_workspace_bytes(B, H, d_c, max_len, 0);
+  int st = mla_absorb_q(q_C, W_UK, qa, dtype, dtype, B, H, d_h, d_c, stream);
+  if (st != MLA_OK) return st;
+  st = mla_decode_partial_warm(qa, q_R, dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, 0, dws, dws_bytes,
+                               W_UV, (size_t)H * d_h * d_c * qe, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine_uv(seq_lens, max_len, B, H, d_c, 0, dws, dws_bytes, W_UV, dtype, d_h, out, ol, lse,
+                               stream);
 }
 
 }  // extern "C"

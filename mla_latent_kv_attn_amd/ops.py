@@ -235,6 +235,55 @@ def mla_uv_out(o_latent: torch.Tensor, W_UV: torch.Tensor, out: Optional[torch.T
     return out
 
 
+def mla_decode_step_workspace_bytes(B: int, H: int, d_c: int, max_len: int) -> int:
+    return int(_lib.lib().mla_decode_step_workspace_bytes(B, H, d_c, max_len))
+
+
+def mla_decode_step_workspace(B: int, H: int, d_c: int, max_len: int, device) -> torch.Tensor:
+    """A zero-filled workspace for mla_decode_step (its flag region must start at zero; every call
+    leaves it zero).  The int32 at byte 0 is the sticky error word of the one-launch form."""
+    n = mla_decode_step_workspace_bytes(B, H, d_c, max_len)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def mla_decode_step_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero the flag region of a step workspace (a fill kernel on the stream)."""
+    _dev(workspace)
+    check("mla_decode_step_init", _lib.lib().mla_decode_step_init(workspace.data_ptr(), workspace.numel(),
+                                                                  _stream(stream, workspace)))
+
+
+def mla_decode_step(q_C, q_R, W_UK, W_UV, cache: Cache, seq_lens, max_len: int, workspace: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, q_abs: Optional[torch.Tensor] = None,
+                    o_latent: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """The whole absorbed decode step (include/mla.h, mla_decode_step): out [B,H,d_h] fp32 from
+    q_C [B,H,d_h], q_R [B,H,d_R], W_UK / W_UV [H,d_h,d_c] and the cache.  q_abs, o_latent and lse
+    are written when given.  ``workspace`` comes from mla_decode_step_workspace (zero-filled)."""
+    _dev(q_C, q_R, W_UK, W_UV, seq_lens, workspace, out, q_abs, o_latent, lse)
+    B, H, d_h = q_C.shape
+    d_R = q_R.shape[2]
+    d_c = W_UK.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h + d_R)
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=q_C.device)
+    for t in (q_C, q_R, W_UK, W_UV, out, q_abs, o_latent, lse):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("mla_decode_step takes contiguous tensors")
+    if q_abs is not None and q_abs.dtype != q_C.dtype:
+        raise ValueError("q_abs has the dtype of q_C")
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    check("mla_decode_step", _lib.lib().mla_decode_step(
+        q_C.data_ptr(), q_R.data_ptr(), W_UK.data_ptr(), W_UV.data_ptr(), dtype_code(q_C), ctypes.byref(cache.desc),
+        seq_lens.data_ptr(), int(max_len), B, H, d_h, d_c, d_R, float(scale), workspace.data_ptr(),
+        workspace.numel(), ptr(q_abs), ptr(o_latent), ptr(lse), out.data_ptr(), _stream(stream, q_C)))
+    return out
+
+
 def mla_cache_append_workspace_bytes(B: int, D: int) -> int:
     return int(_lib.lib().mla_cache_append_workspace_bytes(B, D))
 
