@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of one absorbed MLA decode step on one MI355X.
 
-A step is the whole hot path on one batch: mla_absorb_q -> mla_decode_partial ->
-mla_decode_combine_uv (the combine pass and mla_uv_out; one kernel at batch <= 4), over inputs
-already resident in HBM.  Prints one JSON line.
+A step is the whole hot path on one batch through mla_decode_step, over inputs already resident
+in HBM: one kernel launch for one bf16 sequence at the V3 head sizes (at most 4096 cached tokens),
+otherwise mla_absorb_q -> mla_decode_partial -> mla_decode_combine_uv (the combine pass and
+mla_uv_out; one kernel at batch <= 4).  Prints one JSON line.
 
 Default workload: DeepSeek-V3-shape decode, B=1, H=128, d_c=512, d_R=64, N=4096 cached tokens,
 bf16 caches and weights (``--config 3/4/5`` selects the other synthetic workloads).
@@ -41,6 +42,7 @@ KERNEL_SOURCES = {
     "k_combine_rows": "decode_generic.hip",
     "k_combine_heads": "decode_generic.hip",
     "k_combine_uv": "absorb_uv_mfma.hip",
+    "k_step_b1": "decode_step.hip",
 }
 
 
@@ -60,10 +62,63 @@ def kernel_names(wl):
             "uv": "k_uv_gemv" if small else "k_uv_bf16", "combine_uv": "k_combine_uv"}
 
 
+def one_launch_step(wl, num_splits):
+    """Whether DecodeStep runs the one-launch form of mla_decode_step for this workload (the
+    library's rule for aligned arguments on a GPU with at least 256 compute units)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (num_splits == 0 and wl.dtype == "bf16" and wl.B == 1 and wl.H == 128 and wl.d_h == 128
+            and wl.d_c == 512 and wl.d_R == 64 and wl.n_max <= 4096 and cus >= 256
+            and (wl.layout != "paged" or wl.page_size % 32 == 0))
+
+
+def environment():
+    """GPU name, ROCm / HIP versions and the host CPU model of this run."""
+    import torch
+    env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+           "cus": torch.cuda.get_device_properties(0).multi_processor_count}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    env["cpu_model"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    env["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    env["host_cores"] = len(os.sched_getaffinity(0))
+    return env
+
+
+def sampled_parity(inp, got, n_extra=4, seed=0):
+    """Worst relative L2 over sampled (sequence, head) pairs of the timed run's outputs (o and
+    o_lat) against the oracle: heads 0, 31, 32, 63, 64, 95, 96, 127 (every 32-head block's edges)
+    of the shortest, the longest, the first and a few random sequences."""
+    import numpy as np
+    import oracle
+    wl = inp.wl
+    rng = np.random.default_rng(seed)
+    bs = {0, wl.B - 1, int(np.argmin(inp.lens)), int(np.argmax(inp.lens))}
+    bs |= set(int(x) for x in rng.choice(wl.B, size=min(wl.B, n_extra), replace=False))
+    heads = sorted({h for h in (0, 31, 32, 63, 64, 95, 96, 127) if h < wl.H} | {wl.H - 1})
+    pairs = [(b, h) for b in sorted(bs) if inp.lens[b] > 0 for h in heads]
+    ref = oracle.decode(inp, pairs=pairs)
+    res = {"pairs": len(pairs)}
+    for key in ("o", "o_lat"):
+        res[key] = float(max(oracle.relative_l2(got[key][b, h], ref[key][b, h]) for b, h in pairs)) if pairs else None
+    res["tolerance"] = 1e-5 if wl.dtype == "f32" else 1e-2
+    return res
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=400, help="timed steps (exactly this many)")
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--num-splits", type=int, default=0)
@@ -94,7 +149,8 @@ def source_hash(fname: str) -> str:
     p = os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", fname)
     with open(p, "rb") as f:
         h = hashlib.sha256(f.read())
-    for hdr in ("mla_internal.h", "partial_common.h"):
+    hdrs = ("mla_internal.h", "partial_common.h") + (("step_internal.h",) if fname == "decode_step.hip" else ())
+    for hdr in hdrs:
         with open(os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", hdr), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -230,20 +286,28 @@ def main():
         c = copies[i % R]
         step(c["q_C"], c["q_R"], c["W_UK"], c["W_UV"], caches[i % R], c["lens"])
 
-    # ---------------- whole-step timing (graph of R steps, replayed)
+    # ---------------- whole-step timing: exactly `steps` steps, as replays of a graph of R steps (one
+    # per rotated copy) plus one replay of a graph holding the remaining steps % R
     with torch.cuda.stream(stream):
         for i in range(max(args.warmup, R)):
             one(i)
     torch.cuda.synchronize()
     use_graph = not args.no_graph
+    steps = args.steps
+    spread = None
     if use_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(R):
                 one(i)
+        rem = steps % R
+        g_rem = None
+        if rem:
+            g_rem = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rem, stream=stream):
+                for i in range(rem):
+                    one(i)
         torch.cuda.synchronize()
-        reps = max(1, math.ceil(args.steps / R))
-        steps = reps * R
         with torch.cuda.stream(stream):
             for _ in range(2):
                 g.replay()
@@ -251,12 +315,28 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):          # replay() launches on the current stream
             e0.record(stream)
-            for _ in range(reps):
+            for _ in range(steps // R):
                 g.replay()
+            if g_rem is not None:
+                g_rem.replay()
             e1.record(stream)
         e1.synchronize()
+        # spread: graph replays of R steps timed one by one (outside the timed region)
+        per = []
+        with torch.cuda.stream(stream):
+            for _ in range(max(10, min(40, 4000 // R))):
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                g.replay()
+                a1.record(stream)
+                a1.synchronize()
+                per.append(a0.elapsed_time(a1) / R)
+        per = np.array(per)
+        spread = {"replays": len(per), "steps_per_replay": R,
+                  "ms_per_step_p10": round(float(np.percentile(per, 10)), 6),
+                  "ms_per_step_median": round(float(np.median(per)), 6),
+                  "ms_per_step_p90": round(float(np.percentile(per, 90)), 6)}
     else:
-        steps = args.steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             e0.record(stream)
@@ -266,28 +346,41 @@ def main():
         e1.synchronize()
     ms_per_step = e0.elapsed_time(e1) / steps
     torch.cuda.synchronize()
+    got = {"o": step.out.cpu().numpy().astype(np.float64), "o_lat": step.o_latent.cpu().numpy().astype(np.float64)}
 
     # ---------------- per-kernel durations: HIP events around kernel_reps back-to-back launches of
     # one kernel (rotating input copies, so weights and caches stay cold), on the launch stream
-    names = ["absorb", "partial", "combine_uv"] if fused_combine_uv(wl) else ["absorb", "partial", "combine", "uv"]
+    single = one_launch_step(wl, args.num_splits)
+    if single:
+        names = ["step"]
+    else:
+        names = ["absorb", "partial", "combine_uv"] if fused_combine_uv(wl) else ["absorb", "partial", "combine", "uv"]
     reps = args.kernel_reps
 
     def launch(name, r):
         c = copies[r % R]
-        if name == "absorb":
+        if name == "step":
+            ops.mla_decode_step(c["q_C"], c["q_R"], c["W_UK"], c["W_UV"], caches[r % R], c["lens"], wl.n_max,
+                                step.workspace, out=step.out, q_abs=step.q_abs, o_latent=step.o_latent,
+                                lse=step.lse, scale=step.scale, stream=stream)
+        elif name == "absorb":
             ops.mla_absorb_q(c["q_C"], c["W_UK"], out=step.q_abs, stream=stream)
         elif name == "partial":   # as in the step: spare workgroups (small batch) warm W_UV
             ops.mla_decode_partial_warm(step.q_abs, c["q_R"], caches[r % R], c["lens"], wl.n_max, step.scale,
-                                        step.workspace, c["W_UV"], num_splits=args.num_splits, stream=stream)
+                                        pws, c["W_UV"], num_splits=args.num_splits, stream=stream)
         elif name == "combine":
-            ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, step.workspace, step.o_latent,
+            ops.mla_decode_combine(c["lens"], wl.n_max, wl.B, wl.H, wl.d_c, pws, step.o_latent,
                                    step.lse, num_splits=args.num_splits, stream=stream)
         elif name == "combine_uv":
-            ops.mla_decode_combine_uv(c["lens"], wl.n_max, step.workspace, c["W_UV"], step.o_latent, out=step.out,
+            ops.mla_decode_combine_uv(c["lens"], wl.n_max, pws, c["W_UV"], step.o_latent, out=step.out,
                                       lse=step.lse, num_splits=args.num_splits, stream=stream)
         else:
             ops.mla_uv_out(step.o_latent, c["W_UV"], out=step.out, stream=stream)
 
+    pws = None
+    if not single:
+        pws = torch.empty(max(1, ops.mla_decode_workspace_bytes(wl.B, wl.H, wl.d_c, wl.n_max, args.num_splits)),
+                          dtype=torch.uint8, device=dev)
     kern_us = {}
     with torch.cuda.stream(stream):
         for name in names:
@@ -300,18 +393,25 @@ def main():
             kb.synchronize()
             kern_us[name] = ka.elapsed_time(kb) * 1e3 / reps
     torch.cuda.synchronize()
+    if single:
+        err = int(step.workspace[:4].view(torch.int32)[0].item())
+        if err:
+            raise SystemExit(f"mla_decode_step: a wait between workgroups gave up (error word {err})")
 
     ab, per_tok = alg_bytes(wl, sum_len)
     af = alg_flops(wl, sum_len)
     step_bytes = ab["absorb"] + ab["partial"] + ab["combine"] + ab["uv"]
+    step_flops = af["absorb"] + af["partial"] + af["uv"]
+    ab["step"], af["step"] = step_bytes, step_flops
     value = sum_len / (ms_per_step * 1e-3)
     dom = max(names, key=lambda n: kern_us[n])
-    kname = kernel_names(wl)[dom]
+    kname = "k_step_b1" if single else kernel_names(wl)[dom]
     achieved_gbps = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profiles(kname, wl.name), "alg_bytes_per_launch": ab[dom],
                 "avg_us": round(kern_us[dom], 3)}
+    mfma_name = "step" if single else "partial"
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -326,15 +426,22 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else ("fp8-e4m3 latents, bf16 MFMA" if wl.dtype == "fp8" else "f32"),
         "data": "synthetic (seeded; random-init weights, no trained checkpoint)",
         "config": {"workload": wl.description, "B": wl.B, "H": wl.H, "d_c": wl.d_c, "d_R": wl.d_R,
-                   "sum_len": sum_len, "layout": wl.layout, "num_splits": W, "graph": use_graph,
-                   "input_copies_rotated": R},
+                   "sum_len": sum_len, "layout": wl.layout,
+                   "form": "one launch (mla_decode_step)" if single else "absorb, partial, combine(+uv)",
+                   "num_splits": 32 if single else W, "graph": use_graph, "input_copies_rotated": R},
+        "step_spread": spread,
         "hbm_TBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e12, 3),
         "step_alg_bytes": step_bytes,
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "kernels_frac_of_hbm_peak": {k: round(ab[k] / (kern_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4) for k in names},
-        "partial_mfma_util": round(af["partial"] / (kern_us["partial"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "mfma_util_algorithmic": {"kernel": kname,
+                                  "frac_of_bf16_peak": round(af[mfma_name] / (kern_us[mfma_name] * 1e-6) / 1e12
+                                                             / BF16_PEAK_TFLOPS, 4)},
         "roofline": roofline,
+        "env": environment(),
     }
+    print("[bench] checking the timed run's outputs against the oracle", file=sys.stderr, flush=True)
+    out["rel_l2_sampled"] = sampled_parity(inp, got)
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

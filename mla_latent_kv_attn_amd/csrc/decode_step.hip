@@ -51,8 +51,17 @@ constexpr int kRingBytes = kStepTiles * 4 * kSSlice;   // 147456
 constexpr int kXBytes = 16384;                 // exchange buffer
 constexpr int kLdsBytes = kRingBytes + kXBytes;        // 163840: the whole LDS of a CU
 constexpr int kPRow = 272;                     // bytes per head row of the probabilities (128 tokens + pad)
+constexpr int kLinvOff = 12288;                // exchange-buffer offset of the 1 / l array
 constexpr unsigned kCoh = 16;                  // buffer cache policy: sc1 (device-coherent)
 constexpr uint64_t kWaitTicks = 2000000;       // 20 ms at the 100 MHz s_memrealtime clock
+#ifndef MLA_STEP_FORM
+#define MLA_STEP_FORM 1
+#endif
+#ifndef MLA_STEP_PACE
+#define MLA_STEP_PACE 8
+#endif
+constexpr int kStepForm = MLA_STEP_FORM;       // 1: one launch; 2: absorb kernel + attention kernel
+constexpr int kStepPace = MLA_STEP_PACE;       // s_sleep between the W_UV loads of a loader wave
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
@@ -115,7 +124,121 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 
 }  // namespace
 
-__global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
+// DMA of column slice lw (latent columns 128 lw .. + 127, rope dimensions 16 lw .. + 15) of the
+// 32-token tile t of the sequence into LDS at dst (9216 bytes): latent row q is 256 bytes with its
+// 16-byte chunk c at position c ^ (q & 15), rope row q 32 bytes with chunk c at c ^ ((q >> 3) & 1).
+// Rows past the sequence's end are loaded from its last row (finite data, masked later).
+__device__ __forceinline__ void issue_tile(const StepArgs& a, int t, int len, int lw, uint8_t* dst) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  const int tok0 = t * kTile;
+  const int last = __builtin_amdgcn_readfirstlane(min(kTile, len - tok0) - 1);
+  int64_t lrow0 = 0, rrow0 = 0;
+  int tslot0 = tok0;
+  if (a.block_table) {
+    const int page = load_uniform_i32(a.block_table + tok0 / a.page_size);
+    lrow0 = (int64_t)page * a.lat_sb;
+    rrow0 = (int64_t)page * a.rope_sb;
+    tslot0 = tok0 % a.page_size;
+  }
+  const uint8_t* lbase =
+      (const uint8_t*)uniform_ptr((const uint8_t*)a.latent + (lrow0 + (int64_t)tslot0 * a.lat_st) * 2 + 256 * lw);
+  const uint8_t* rbase =
+      (const uint8_t*)uniform_ptr((const uint8_t*)a.rope + (rrow0 + (int64_t)tslot0 * a.rope_st) * 2 + 32 * lw);
+  const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+  const uint32_t lstride = (uint32_t)a.lat_st * 2u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = 4 * k + (ln >> 4);
+    const uint32_t voff = (uint32_t)min(q, last) * lstride + 16u * (uint32_t)((ln & 15) ^ (q & 15));
+    lds_dma16(lbase, voff, st + 1024 * k);
+  }
+  const int rq = ln >> 1;
+  const uint32_t roff =
+      (uint32_t)(min(rq, last) * (int)a.rope_st * 2) + 16u * (uint32_t)((ln & 1) ^ ((rq >> 3) & 1));
+  lds_dma16(rbase, roff, st + kSRope);
+}
+
+// Phase A, compute wave `wave` of workgroup r: q'[hw][c0 .. c0 + 63] with hw = 32 wave + r / 8 and
+// c0 = 64 (r % 8) (the 16 KB piece of W_UK[hw]); lane (rg, cc) sums rows 16 rg .. 16 rg + 15 of
+// columns c0 + 8 cc .. + 7.  xq: 256 bytes of LDS private to the wave.  `publish`: the one-launch
+// form, which hands the piece to the attention workgroups through flags.
+__device__ __forceinline__ void absorb_piece(const StepArgs& a, int r, int wave, int lane, uint8_t* xq, bool publish) {
+  {
+    const int hw = 32 * wave + (r >> 3);
+    const int c0 = (r & 7) * 64;
+    const int rg = lane >> 3, cc = lane & 7;
+    u32x4 qv = {0u, 0u, 0u, 0u};
+    if (lane < 16) qv = *(const u32x4*)(a.q_C + hw * 128 + lane * 8);
+    u32x4 wv[16];
+    const uint16_t* wp = a.W_UK + ((int64_t)hw * 128 + 16 * rg) * 512 + c0 + cc * 8;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) wv[k] = *(const u32x4*)(wp + k * 512);
+    if (lane < 16) *(u32x4*)(xq + lane * 16) = qv;
+    const u32x4 qa = *(const u32x4*)(xq + 32 * rg), qb = *(const u32x4*)(xq + 32 * rg + 16);
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t qw = k < 8 ? qa[(k & 7) >> 1] : qb[(k & 7) >> 1];
+      const float q = (k & 1) ? bf16_hi(qw) : bf16_lo(qw);
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        acc[2 * c2] = fmaf(q, bf16_lo(wv[k][c2]), acc[2 * c2]);
+        acc[2 * c2 + 1] = fmaf(q, bf16_hi(wv[k][c2]), acc[2 * c2 + 1]);
+      }
+    }
+    // lane (rg, cc) now holds column c0 + 8 cc + rg; lanes with rg even store two columns
+    const float s = sum8_over_bits543(acc, lane);
+    const float s1 = __shfl_xor(s, 8, 64);
+    if (!publish) {
+      if ((rg & 1) == 0) *(uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg) = pack_bf16x2(s, s1);
+      return;
+    }
+    // one launch: device-coherent store, completed before one flag per consumer is set (compute
+    // wave cw = (r % 8) / 2 of each attention workgroup of head block `wave`, producer index
+    // 2 (r / 8) + r % 2 among its 64 producers)
+    if ((rg & 1) == 0)
+      __hip_atomic_store((uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg), pack_bf16x2(s, s1), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    if (lane < kStepSplits) {
+      const int cw = (r & 7) >> 1, p = 2 * (r >> 3) + (r & 1);
+      coh_store_i32(a.fa + ((wave * kStepSplits + lane) * 4 + cw) * 64 + p, 1);
+    }
+  }
+}
+
+// Absorb kernel: q'[h] = W_UK[h]^T q_C[h] for all heads, 64 columns of four heads per workgroup
+// (one head per compute wave), and, on the side, the cache tiles that the attention kernel's
+// workgroups on this XCD read first are pulled into this XCD's L2.
+__global__ __launch_bounds__(512) void k_step_absorb(StepArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kSSlice + 1024];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* xb = lds + 4 * kSSlice;
+  if (wave >= 4) {
+    // tile (r / 8) / 4 of split 4 (r % 8) + (r / 8) % 4: the attention workgroups of that split
+    // run on this workgroup's XCD (r % 8) in the next kernel
+    const int slot = r >> 3;
+    if (slot >= 16) return;
+    const int split = 4 * (r & 7) + (slot & 3), i = slot >> 2;
+    const int len = max(load_uniform_i32(a.seq_lens), 0);
+    const int T = min(tiles_of(len), kStepSplits * kStepTiles);
+    const int t0 = split * T / kStepSplits, ntl = (split + 1) * T / kStepSplits - t0;
+    if (i < ntl) issue_tile(a, t0 + i, len, wave - 4, lds + (wave - 4) * kSSlice);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    return;
+  }
+  absorb_piece(a, r, wave, lane, xb + wave * 256, false);
+}
+
+template <bool ONE, int PACE>
+__global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,45 +262,12 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     const int lw = wave - 4;
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    if (ONE) lds_barrier();   // B0: the compute waves have published their q' pieces
     if (attn) {
       const int len = max(load_uniform_i32(a.seq_lens), 0);
       int t0, ntl;
       tile_range(len, t0, ntl);
-      const uint32_t lstride = (uint32_t)a.lat_st * 2u;
-      for (int i = 0; i < ntl; ++i) {
-        const int tok0 = (t0 + i) * kTile;
-        const int last = __builtin_amdgcn_readfirstlane(min(kTile, len - tok0) - 1);
-        int64_t lrow0, rrow0;
-        int tslot0;
-        if (a.block_table) {
-          const int page = load_uniform_i32(a.block_table + tok0 / a.page_size);
-          lrow0 = (int64_t)page * a.lat_sb;
-          rrow0 = (int64_t)page * a.rope_sb;
-          tslot0 = tok0 % a.page_size;
-        } else {
-          lrow0 = 0;
-          rrow0 = 0;
-          tslot0 = tok0;
-        }
-        const uint8_t* lbase = (const uint8_t*)uniform_ptr((const uint8_t*)a.latent +
-                                                           (lrow0 + (int64_t)tslot0 * a.lat_st) * 2 + 256 * lw);
-        const uint8_t* rbase = (const uint8_t*)uniform_ptr((const uint8_t*)a.rope +
-                                                           (rrow0 + (int64_t)tslot0 * a.rope_st) * 2 + 32 * lw);
-        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_addr(lds + (i * 4 + lw) * kSSlice));
-        // latent row q of the slice: 256 bytes, 16-byte chunk c at position c ^ (q & 15); rows past
-        // the sequence's end are loaded from its last row (finite data, masked later)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int q = 4 * k + (ln >> 4);
-          const uint32_t voff = (uint32_t)min(q, last) * lstride + 16u * (uint32_t)((ln & 15) ^ (q & 15));
-          lds_dma16(lbase, voff, st + 1024 * k);
-        }
-        // rope row q: 32 bytes, chunk c at position c ^ ((q >> 3) & 1)
-        const int rq = ln >> 1;
-        const uint32_t roff =
-            (uint32_t)(min(rq, last) * (int)a.rope_st * 2) + 16u * (uint32_t)((ln & 1) ^ ((rq >> 3) & 1));
-        lds_dma16(rbase, roff, st + kSRope);
-      }
+      for (int i = 0; i < ntl; ++i) issue_tile(a, t0 + i, len, lw, lds + (i * 4 + lw) * kSSlice);
     } else {
       // W_UV[h]: row i (1 KB) at LDS i * 1024, 16-byte chunk c at position c ^ (i & 63)
       const uint8_t* wbase = (const uint8_t*)a.W_UV + (int64_t)hproj * 128 * 1024;
@@ -185,6 +275,7 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
         const int i = 32 * lw + k;
         lds_dma16(wbase + i * 1024, 16u * (uint32_t)(ln ^ (i & 63)),
                   __builtin_amdgcn_readfirstlane(lds_addr(lds + i * 1024)));
+        if (PACE > 0) __builtin_amdgcn_s_sleep(PACE);
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -202,52 +293,10 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     return;
   }
 
-  // ------------------------------------------------------------------ phase A: absorb piece
-  // compute wave w: q'[hw][c0 .. c0 + 63], hw = 32 w + r / 8, c0 = 64 (r % 8); lane (rg, cc) sums
-  // rows 16 rg .. 16 rg + 15 of columns c0 + 8 cc .. + 7
-  {
-    const int hw = 32 * wave + (r >> 3);
-    const int c0 = (r & 7) * 64;
-    const int rg = lane >> 3, cc = lane & 7;
-    u32x4 qv = {0u, 0u, 0u, 0u};
-    if (lane < 16) qv = *(const u32x4*)(a.q_C + hw * 128 + lane * 8);
-    u32x4 wv[16];
-    const uint16_t* wp = a.W_UK + ((int64_t)hw * 128 + 16 * rg) * 512 + c0 + cc * 8;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) wv[k] = *(const u32x4*)(wp + k * 512);
-    uint8_t* xq = xb + wave * 256;
-    if (lane < 16) *(u32x4*)(xq + lane * 16) = qv;
-    const u32x4 qa = *(const u32x4*)(xq + 32 * rg), qb = *(const u32x4*)(xq + 32 * rg + 16);
-    float acc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t qw = k < 8 ? qa[(k & 7) >> 1] : qb[(k & 7) >> 1];
-      const float q = (k & 1) ? bf16_hi(qw) : bf16_lo(qw);
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) {
-        acc[2 * c2] = fmaf(q, bf16_lo(wv[k][c2]), acc[2 * c2]);
-        acc[2 * c2 + 1] = fmaf(q, bf16_hi(wv[k][c2]), acc[2 * c2 + 1]);
-      }
-    }
-    // lane (rg, cc) now holds column c0 + 8 cc + rg; lanes with rg even store two columns
-    const float s = sum8_over_bits543(acc, lane);
-    const float s1 = __shfl_xor(s, 8, 64);
-    if ((rg & 1) == 0)
-      __hip_atomic_store((uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg), pack_bf16x2(s, s1), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    compiler_fence();
-    // one flag per consumer: compute wave cw = (r % 8) / 2 of each attention workgroup of head
-    // block `wave`, producer index 2 (r / 8) + r % 2 among its 64 producers
-    if (lane < kStepSplits) {
-      const int cw = (r & 7) >> 1, p = 2 * (r >> 3) + (r & 1);
-      coh_store_i32(a.fa + ((wave * kStepSplits + lane) * 4 + cw) * 64 + p, 1);
-    }
+  if (ONE) {
+    absorb_piece(a, r, wave, lane, xb + wave * 256, true);
+    lds_barrier();   // B0
   }
-
   const int len = max(load_uniform_i32(a.seq_lens), 0);
   if (attn) {
     // ---------------------------------------------------------------- phase B: attention
@@ -256,7 +305,8 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     int t0, ntl;
     tile_range(len, t0, ntl);
     // this wave's folded-query slice: latent k-steps 8 cw .. 8 cw + 7 (qf[0..7]) and rope k-step cw
-    wait_flags(a.fa + ((g * kStepSplits + split) * 4 + cw) * 64, lane, 64, a.err);
+    // (one launch: after the flags of its 64 producers)
+    if (ONE) wait_flags(a.fa + ((g * kStepSplits + split) * 4 + cw) * 64, lane, 64, a.err);
     const __amdgpu_buffer_rsrc_t qr = rsrc(a.qp);
     u32x4 qf[9];
 #pragma unroll
@@ -270,19 +320,29 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     const int srow = pi_row(hl);
     const int sc_row = srow * 256, sc_x = srow & 15;
     const int rope_rd = kSRope + srow * 32 + 16 * (hf ^ ((srow >> 3) & 1));
+    // The four tiles' chains advance together, one k-step at a time, with the next k-step's
+    // operands read ahead (tiles past ntl read stale, in-bounds LDS; their scores are never used)
     f32x16 S[kStepTiles];
 #pragma unroll
-    for (int i = 0; i < kStepTiles; ++i) {
-      S[i] = f32x16{};
-      if (i < ntl) {
-        const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
-        u32x4 av[8];
+    for (int i = 0; i < kStepTiles; ++i) S[i] = f32x16{};
+    auto a_op = [&](int i, int j) __attribute__((always_inline)) -> u32x4 {
+      const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+      return j < 8 ? *(const u32x4*)(st + sc_row + 16 * ((2 * j + hf) ^ sc_x)) : *(const u32x4*)(st + rope_rd);
+    };
+    {
+      u32x4 cur[kStepTiles], nxt[kStepTiles];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] = *(const u32x4*)(st + sc_row + 16 * ((2 * j + hf) ^ sc_x));
-        const u32x4 rv = *(const u32x4*)(st + rope_rd);
+      for (int i = 0; i < kStepTiles; ++i) cur[i] = a_op(i, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) S[i] = mfma32x32x16(av[j], qf[j], S[i]);
-        S[i] = mfma32x32x16(rv, qf[8], S[i]);
+      for (int j = 0; j < 9; ++j) {
+        if (j < 8) {
+#pragma unroll
+          for (int i = 0; i < kStepTiles; ++i) nxt[i] = a_op(i, j + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < kStepTiles; ++i) S[i] = mfma32x32x16(cur[i], qf[j], S[i]);
+#pragma unroll
+        for (int i = 0; i < kStepTiles; ++i) cur[i] = nxt[i];
       }
     }
     // add the four waves' partials, one tile per round: wave w writes its block head-major (128 B
@@ -334,65 +394,77 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     l += __shfl_xor(l, 1, 64);
     l += __shfl_xor(l, 2, 64);
     l += __shfl_xor(l, 4, 64);
-    if (sc == 0)
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m), __float_as_uint(l)}, rsrc(a.part_ml),
-                                            (int)((split * 128 + 32 * g + sn) * 8), 0, kCoh);
-    lds_barrier();   // the probabilities of all 32 heads are in LDS
+    float* linv = (float*)(xb + kLinvOff);   // [32] 1 / l per head (0 for a split without tokens)
+    if (sc == 0) linv[sn] = l > 0.f ? 1.f / l : 0.f;
+    lds_barrier();   // the probabilities and 1 / l of all 32 heads are in LDS
 
-    // value: acc[cb] = O^T block (latent columns 128 cw + 32 cb .. + 31) x (32 heads)
+    // value: acc[cb] = O^T block (latent columns 128 cw + 32 cb .. + 31) x (32 heads); step
+    // 2 i + ks takes tokens 16 ks .. 16 ks + 15 of tile i, its operands read one step ahead
     if (ntl > 0) {
       const int G = lane >> 4;
       const int vrow0 = 8 * (G >> 1) + ((lane & 15) >> 2);
+      auto v_ops = [&](int stp, u32x4 (&av)[4], u32x4& pv) __attribute__((always_inline)) {
+        const int i = min(stp >> 1, kStepTiles - 1), ks = stp & 1;
+        const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+        pv = *(const u32x4*)(xb + hl * kPRow + 2 * (kTile * i + 16 * ks + 8 * hf));
+        const int R = 16 * ks + vrow0;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int cch = 4 * cb + 2 * (G & 1) + ((lane & 3) >> 1);
+          const uint8_t* pa = st + R * 256 + 16 * (cch ^ (R & 15)) + 8 * (lane & 1);
+          const uint8_t* pb = st + (R + 4) * 256 + 16 * (cch ^ ((R + 4) & 15)) + 8 * (lane & 1);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pb));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          av[cb] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+      };
       f32x16 acc[4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
+      u32x4 ca[4], na[4], cp, np;
+      v_ops(0, ca, cp);
 #pragma unroll
-      for (int i = 0; i < kStepTiles; ++i) {
-        if (i < ntl) {
-          const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+      for (int stp = 0; stp < 2 * kStepTiles; ++stp) {
+        if (stp + 1 < 2 * kStepTiles) v_ops(stp + 1, na, np);
+        if ((stp >> 1) < ntl) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 pv = *(const u32x4*)(xb + hl * kPRow + 2 * (kTile * i + 16 * ks + 8 * hf));
-            const int R = 16 * ks + vrow0;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-              const int cch = 4 * cb + 2 * (G & 1) + ((lane & 3) >> 1);
-              const uint8_t* pa = st + R * 256 + 16 * (cch ^ (R & 15)) + 8 * (lane & 1);
-              const uint8_t* pb = st + (R + 4) * 256 + 16 * (cch ^ ((R + 4) & 15)) + 8 * (lane & 1);
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
-              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pb));
-              const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-              acc[cb] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pv, acc[cb]);
-            }
-          }
+          for (int cb = 0; cb < 4; ++cb) acc[cb] = mfma32x32x16(ca[cb], cp, acc[cb]);
         }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) ca[cb] = na[cb];
+        cp = np;
       }
-      // partial rows to the workspace: each 32 x 32 block is turned into head rows through this
-      // wave's own ring slices (no other wave reads them), then stored as whole 128-byte lines
+      // partial rows to the workspace as bf16 acc / l (the split's softmax-weighted latent mean):
+      // each 32 x 32 block is turned into head rows of 64 bytes through this wave's own ring
+      // slice (no other wave reads it; 16-byte chunk c of row n at position c ^ (n & 3)), then
+      // stored as 16-byte pieces of whole rows (a store of pieces scattered over 32 rows per
+      // lane pair issues far more slowly)
+      const float li = linv[hl];
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      const int trow = ln >> 3, tch = ln & 7;
-      const int xs = ((ln & 31) >> 1) & 7;
-      const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+      uint8_t* tb = lds + cw * kSSlice;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        uint8_t* tb = lds + ((cb >> 1) * 4 + cw) * kSSlice + (cb & 1) * 4096;
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
-          *(f32x4*)(tb + (ln & 31) * 128 + 16 * ((2 * v4 + (ln >> 5)) ^ xs)) =
-              f32x4{acc[cb][4 * v4], acc[cb][4 * v4 + 1], acc[cb][4 * v4 + 2], acc[cb][4 * v4 + 3]};
-      }
+          *(u32x2*)(tb + cb * 2048 + hl * 64 + 16 * (v4 ^ (hl & 3)) + 8 * hf) =
+              u32x2{pack_bf16x2(acc[cb][4 * v4] * li, acc[cb][4 * v4 + 1] * li),
+                    pack_bf16x2(acc[cb][4 * v4 + 2] * li, acc[cb][4 * v4 + 3] * li)};
+      const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+      const int tc = ln & 3;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint8_t* tb = lds + ((cb >> 1) * 4 + cw) * kSSlice + (cb & 1) * 4096;
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = 8 * q + trow;
-          const u32x4 v = *(const u32x4*)(tb + row * 128 + 16 * (tch ^ ((row >> 1) & 7)));
-          coh_store4(pr, (uint32_t)(((split * 128 + 32 * g + row) * 512 + 128 * cw + 32 * cb + 4 * tch) * 4), v);
+        for (int ps = 0; ps < 2; ++ps) {
+          const int row = (ln >> 2) + 16 * ps;
+          const u32x4 v = *(const u32x4*)(tb + cb * 2048 + row * 64 + 16 * (tc ^ (row & 3)));
+          coh_store4(pr, (uint32_t)(((split * 128 + 32 * g + row) * 512 + 128 * cw + 32 * cb + 8 * tc) * 2), v);
         }
-      }
     }
+    if (sc == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m), __float_as_uint(l)}, rsrc(a.part_ml),
+                                            (int)((split * 128 + 32 * g + sn) * 8), 0, kCoh);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     compiler_fence();
@@ -406,13 +478,21 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
   if (wave == 0) wait_flags(a.fb + h * kStepSplits, lane, kStepSplits, a.err);
   lds_barrier();   // B1: W_UV[h] in LDS, every split of head h published
   float* ws = (float*)(xb + 1024);        // [32] split weights
-  float* ol = (float*)(xb + 2048);        // [512] o_lat[h]
+  uint16_t* olhi = (uint16_t*)(xb + 2048);   // [512] bf16 hi part of o_lat[h]
+  uint16_t* ollo = (uint16_t*)(xb + 3072);   // [512] bf16 lo part
   float* half1 = (float*)(xb + 4096);     // [128] float4: the second half's sums
   float* stat = (float*)(xb + 8192);      // M, L
+  // the partial rows of the 32 splits are loaded first (all in flight together), the splits'
+  // (m, l) pairs by wave 0 just before them; the weights are ready before the rows have landed
+  const int c4 = tid & 127, hs = tid >> 7;
+  u32x2 ml = {0u, 0u};
+  if (wave == 0 && lane < kStepSplits) ml = coh_load2(rsrc(a.part_ml), (uint32_t)((lane * 128 + h) * 8));
+  const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+  u32x2 x[kStepSplits / 2];
+#pragma unroll
+  for (int u = 0; u < kStepSplits / 2; ++u)
+    x[u] = coh_load2(pr, (uint32_t)((((hs + 2 * u) * 128 + h) * 512 + 4 * c4) * 2));
   if (wave == 0) {
-    // (m, l) of the splits: lane s < 32
-    u32x2 ml = {0u, 0u};
-    if (lane < kStepSplits) ml = coh_load2(rsrc(a.part_ml), (uint32_t)((lane * 128 + h) * 8));
     const float ms = lane < kStepSplits ? __uint_as_float(ml[0]) : -INFINITY;
     const float ls = lane < kStepSplits ? __uint_as_float(ml[1]) : 0.f;
     float M = ms;
@@ -422,26 +502,23 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     float L = w * ls;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d, 64);
-    if (lane < kStepSplits) ws[lane] = w;
+    // split s contributes l_s 2^(m_s - M) / L times its mean acc_s / l_s
+    if (lane < kStepSplits) ws[lane] = L > 0.f ? w * ls / L : 0.f;
     if (lane == 0) {
       stat[0] = M;
       stat[1] = L;
     }
   }
   lds_barrier();
+  // o_latent and lse are stored at the very end: a store in flight before the MFMA work below
+  // would make the compiler wait for it before reusing its registers
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   {
     // thread t: columns 4 (t % 128) .. + 3 over splits t / 128 + 2 u
-    const int c4 = tid & 127, hs = tid >> 7;
-    const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
-    u32x4 x[kStepSplits / 2];
-#pragma unroll
-    for (int u = 0; u < kStepSplits / 2; ++u)
-      x[u] = coh_load4(pr, (uint32_t)((((hs + 2 * u) * 128 + h) * 512 + 4 * c4) * 4));
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kStepSplits / 2; ++u) {
       const float w = ws[hs + 2 * u];
-      const f32x4 xv = __builtin_bit_cast(f32x4, x[u]);
+      const f32x4 xv = {bf16_lo(x[u][0]), bf16_hi(x[u][0]), bf16_lo(x[u][1]), bf16_hi(x[u][1])};
       // a split without tokens has weight 0 and never wrote its rows: select, do not multiply
       if (w != 0.f) o += w * xv;
     }
@@ -449,38 +526,56 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     lds_barrier();
     if (hs == 0) {
       o += *(const f32x4*)(half1 + 4 * c4);
-      const float M = stat[0], L = stat[1];
-      const float inv = M == -INFINITY ? 0.f : 1.f / L;
-      o *= inv;
-      *(f32x4*)(ol + 4 * c4) = o;
-      if (a.o_latent) *(f32x4*)(a.o_latent + h * 512 + 4 * c4) = o;
-      if (a.lse && tid == 0) a.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * 0.69314718055994530942f;
+
+      // o_lat split into bf16 hi + lo parts for the W_UV product below
+      const uint32_t h01 = pack_bf16x2(o[0], o[1]), h23 = pack_bf16x2(o[2], o[3]);
+      const uint32_t l01 = pack_bf16x2(o[0] - bf16_lo(h01), o[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16x2(o[2] - bf16_lo(h23), o[3] - bf16_hi(h23));
+      *(u32x2*)(olhi + 4 * c4) = u32x2{h01, h23};
+      *(u32x2*)(ollo + 4 * c4) = u32x2{l01, l23};
     }
     lds_barrier();
   }
   {
-    // out[h][i] = sum_k W_UV[h][i][k] o_lat[k]: thread t takes row i = t / 2, columns
-    // 256 (t % 2) .. + 255 (32 chunks of 8), W from LDS (chunk c of row i at c ^ (i & 63))
-    const int i = tid >> 1, kh = tid & 1;
-    const uint8_t* wr = lds + i * 1024;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < 32; ++q) {
-      const int c = 32 * kh + q;
-      const u32x4 wv = *(const u32x4*)(wr + 16 * (c ^ (i & 63)));
-      const f32x4 xa = *(const f32x4*)(ol + 8 * c), xc = *(const f32x4*)(ol + 8 * c + 4);
-      s0 = fmaf(bf16_lo(wv[0]), xa[0], s0);
-      s1 = fmaf(bf16_hi(wv[0]), xa[1], s1);
-      s0 = fmaf(bf16_lo(wv[1]), xa[2], s0);
-      s1 = fmaf(bf16_hi(wv[1]), xa[3], s1);
-      s0 = fmaf(bf16_lo(wv[2]), xc[0], s0);
-      s1 = fmaf(bf16_hi(wv[2]), xc[1], s1);
-      s0 = fmaf(bf16_lo(wv[3]), xc[2], s0);
-      s1 = fmaf(bf16_hi(wv[3]), xc[3], s1);
+    // out[h][i] = sum_k W_UV[h][i][k] o_lat[k] on MFMA 16x16x32 (bf16): wave w takes rows
+    // 32 w .. 32 w + 31 (two 16-row blocks).  A = W_UV rows from LDS (chunk c of row i at
+    // position c ^ (i & 63)); B = o_lat split into bf16 hi (column 0) and lo (column 1) parts
+    // (from LDS), zero elsewhere, so that out = D[:, 0] + D[:, 1] keeps about 16 bits of o_lat.
+    const int n = lane & 15, kq = lane >> 4;
+    const uint16_t* bsrc = n == 0 ? olhi : ollo;
+    u32x4 bq[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const u32x4 v = *(const u32x4*)(bsrc + 32 * st + 8 * kq);
+      bq[st] = n < 2 ? v : u32x4{0u, 0u, 0u, 0u};
     }
-    float t = s0 + s1;
-    t += __shfl_xor(t, 1, 64);
-    if (kh == 0) a.out[h * 128 + i] = t;
+    f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+    const int i0 = 32 * wave + n, i1 = i0 + 16;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int c = 4 * st + kq;
+      const u32x4 w0 = *(const u32x4*)(lds + i0 * 1024 + 16 * (c ^ (i0 & 63)));
+      const u32x4 w1 = *(const u32x4*)(lds + i1 * 1024 + 16 * (c ^ (i1 & 63)));
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0), __builtin_bit_cast(bf16x8, bq[st]),
+                                                   d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1), __builtin_bit_cast(bf16x8, bq[st]),
+                                                   d1, 0, 0, 0);
+    }
+    // lane (n, kq) holds rows 4 kq + e (e = 0..3) of each block, column n: add columns 0 and 1
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d0[e] += __shfl_xor(d0[e], 1, 64);
+      d1[e] += __shfl_xor(d1[e], 1, 64);
+    }
+    if (n == 0) {
+      *(f32x4*)(a.out + h * 128 + 32 * wave + 4 * kq) = d0;
+      *(f32x4*)(a.out + h * 128 + 32 * wave + 16 + 4 * kq) = d1;
+    }
+  }
+  if (hs == 0 && a.o_latent) *(f32x4*)(a.o_latent + h * 512 + 4 * c4) = o;
+  if (a.lse && tid == 0) {
+    const float M = stat[0], L = stat[1];
+    a.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * 0.69314718055994530942f;
   }
 }
 
@@ -491,7 +586,14 @@ __global__ void k_step_zero(int* p, int64_t n) {
 }
 
 hipError_t launch_step_b1(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_step_b1, dim3(kStepWGs), dim3(512), 0, s, a);
+  if (kStepForm == 1) {
+    hipLaunchKernelGGL((k_step_attend<true, kStepPace>), dim3(kStepWGs), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_step_absorb, dim3(kStepWGs), dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_step_attend<false, kStepPace>), dim3(kStepWGs), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

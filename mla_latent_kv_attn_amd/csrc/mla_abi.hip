@@ -428,7 +428,7 @@ int mla_decode_step(const void* q_C, const void* q_R, const void* W_UK, const vo
     a.fb = a.fa + mla::kStepFaInts;
     a.qp = q_abs ? (uint16_t*)q_abs : (uint16_t*)data;
     a.part_ml = (float*)(data + round256(mla::kStepQpBytes));
-    a.part_acc = (float*)(data + round256(mla::kStepQpBytes) + round256(mla::kStepMlBytes));
+    a.part_acc = (uint16_t*)(data + round256(mla::kStepQpBytes) + round256(mla::kStepMlBytes));
     a.out = out;
     a.o_latent = o_latent;
     a.lse = lse;

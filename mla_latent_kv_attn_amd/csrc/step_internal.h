@@ -23,7 +23,7 @@ struct StepArgs {
   float sl2;                    // softmax scale * log2(e)
   uint16_t* qp;                 // [128, 512] bf16 folded query (written, then read by other workgroups)
   float* part_ml;               // [kStepSplits, 128, 2]
-  float* part_acc;              // [kStepSplits, 128, 512]
+  uint16_t* part_acc;           // [kStepSplits, 128, 512] bf16 acc / l of each split
   int* fa;                      // [4, kStepSplits, 4, 64] flags: q' pieces
   int* fb;                      // [128, kStepSplits] flags: split partials
   int* err;                     // sticky error word: a wait gave up
@@ -40,7 +40,7 @@ constexpr size_t kStepFbInts = (size_t)128 * kStepSplits;
 constexpr size_t kStepFlagBytes = kStepErrBytes + (kStepFaInts + kStepFbInts) * 4;
 constexpr size_t kStepQpBytes = (size_t)128 * 512 * 2;
 constexpr size_t kStepMlBytes = (size_t)kStepSplits * 128 * 2 * 4;
-constexpr size_t kStepAccBytes = (size_t)kStepSplits * 128 * 512 * 4;
+constexpr size_t kStepAccBytes = (size_t)kStepSplits * 128 * 512 * 2;
 
 hipError_t launch_step_b1(const StepArgs& a, hipStream_t s);
 hipError_t launch_step_zero(int* p, int64_t n, hipStream_t s);
