@@ -223,6 +223,30 @@ int mla_decode_combine_uv(const int32_t* seq_lens, int max_len, int B, int H, in
                           float* out, float* o_latent, float* lse, void* stream);
 
 /*
+ * mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results without the workspace, which is instead a fixed array of
+ * mla_decode_attn_noalloc_max_bytes() bytes (64 MiB) that the library holds on each device it
+ * runs on until the process ends.  No memory is allocated by the call.
+ *   num_splits 0 = the library's choice, mla_decode_attn_noalloc_splits(B, H, d_c, max_len): the
+ *              split count mla_decode_attn would use, lowered until its workspace fits the array;
+ *              an explicit count is used as given.
+ * Returns MLA_ERR_WORKSPACE when the workspace of these sizes and split count exceeds the array
+ * (with the V3 head count, slots = splits + B - 1 of 256 KB each, so at most 256 slots), other
+ * errors as for mla_decode_attn.  The first call on a device looks up the array's address on that
+ * device (hipGetSymbolAddress); a failure there returns MLA_ERR_HIP.
+ * Every call on one device uses that device's one array, which keeps the last call's contents
+ * (the decode passes need no particular initial contents): calls that overlap in time on one
+ * device, for example on two streams, race and give undefined results.
+ * Results are those of mla_decode_attn with the same split count.
+ */
+size_t mla_decode_attn_noalloc_max_bytes(void);
+int mla_decode_attn_noalloc_splits(int B, int H, int d_c, int max_len);
+int mla_decode_attn_noalloc(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                            const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                            int num_splits, float* o_latent, float* lse, void* stream);
+
+/*
  * mla_uv_out -- apply W_UV once to the weighted latent sum ("Grouped-query and
  * latent attention", section "The absorption trick": sum_j a_j W_UV c_j =
  * W_UV sum_j a_j c_j).

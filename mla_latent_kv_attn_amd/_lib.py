@@ -78,6 +78,12 @@ _SIGS = {
                                              ctypes.c_void_p, ctypes.c_void_p]),
     "mla_uv_out": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "mla_decode_attn_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "mla_decode_attn_noalloc_splits": (ctypes.c_int, [ctypes.c_int] * 4),
+    "mla_decode_attn_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(CacheDesc),
+                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p]),
     "mla_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "mla_decode_step_init": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_decode_step": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.POINTER(CacheDesc),

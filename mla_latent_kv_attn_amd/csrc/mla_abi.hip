@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rows_internal.h"
 #include "step_internal.h"
@@ -282,6 +283,73 @@ int mla_decode_attn(const void* q_abs, const void* q_R, int q_dtype, const mla_c
   st = launch_partial(pa, generic, fp8, paged, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   return hip_status(mla::launch_combine(ca, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// mla_decode_attn_noalloc: mla_decode_attn with its workspace in a device array of this file
+// (each device holds its own copy; its address is taken once per device at the first call).
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];   // device address of `scratch` per device, null = not taken yet
+
+// The device address of the current device's scratch array (hipGetSymbolAddress once per device,
+// with that device current).  The array's name is a host-side stand-in in host code, never an
+// address to pass to a kernel.
+int current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kScratchDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_attn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int mla_decode_attn_noalloc_splits(int B, int H, int d_c, int max_len) {
+  if (B < 1 || H < 1 || d_c < 1 || max_len < 0) return 0;
+  int W = auto_splits(B, H, max_len);
+  while (W > 1 && mla::ws_total_bytes(W, B, H, d_c) > kNoAllocScratchBytes) --W;
+  return mla::ws_total_bytes(W, B, H, d_c) <= kNoAllocScratchBytes ? W : 0;
+}
+
+int mla_decode_attn_noalloc(const void* q_abs, const void* q_R, int q_dtype, const mla_cache_desc* cache,
+                            const int32_t* seq_lens, int max_len, int B, int H, int d_c, int d_R, float scale,
+                            int num_splits, float* o_latent, float* lse, void* stream) {
+  if (B < 0 || H < 1 || d_c < 4 || max_len < 0 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (B == 0) return mla_decode_attn(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale,
+                                     num_splits, nullptr, 0, o_latent, lse, stream);
+  int W = num_splits;
+  if (W == 0) {
+    W = mla_decode_attn_noalloc_splits(B, H, d_c, max_len);
+    if (W == 0) return MLA_ERR_WORKSPACE;   // even one split needs more than the array holds
+  }
+  if (mla::ws_total_bytes(W, B, H, d_c) > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = current_scratch(&ws);
+  if (st != MLA_OK) return st;
+  return mla_decode_attn(q_abs, q_R, q_dtype, cache, seq_lens, max_len, B, H, d_c, d_R, scale, W, ws,
+                         kNoAllocScratchBytes, o_latent, lse, stream);
 }
 
 int mla_uv_out(const float* o_latent, const void* W_UV, int w_dtype, float* out, int B, int H, int d_h, int d_c,

@@ -156,6 +156,26 @@ def mla_decode_attn(q_abs: torch.Tensor, q_R: torch.Tensor, cache: Cache, seq_le
     return o_latent, lse
 
 
+def mla_decode_attn_noalloc(q_abs: torch.Tensor, q_R: torch.Tensor, cache: Cache, seq_lens: torch.Tensor,
+                            max_len: int, o_latent: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, d_h: Optional[int] = None, num_splits: int = 0,
+                            stream=None):
+    """mla_decode_attn with the library's fixed device array as its workspace (include/mla.h):
+    writes o_latent [B,H,d_c] (and lse [B,H]); allocates nothing, so o_latent is required."""
+    _dev(q_abs, q_R, seq_lens, o_latent, lse)
+    B, H, d_c = q_abs.shape
+    d_R = q_R.shape[2]
+    if scale is None:
+        if d_h is None:
+            raise ValueError("pass scale or d_h")
+        scale = 1.0 / math.sqrt(d_h + d_R)
+    check("mla_decode_attn_noalloc", _lib.lib().mla_decode_attn_noalloc(
+        q_abs.data_ptr(), q_R.data_ptr(), dtype_code(q_abs), ctypes.byref(cache.desc), seq_lens.data_ptr(),
+        int(max_len), B, H, d_c, d_R, float(scale), int(num_splits), o_latent.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(stream, q_abs)))
+    return o_latent, lse
+
+
 def mla_decode_attn_raw(q_abs, q_R, cache: Cache, seq_lens, max_len, scale, num_splits, workspace, o_latent, lse,
                         stream=None) -> int:
     """Direct call; returns the status code (used by error-path tests)."""
