@@ -8,28 +8,32 @@
 // ("Grouped-query and latent attention", sections "The absorption trick" and "Why a separate
 // rotary key".)  At one sequence the step moves 33.5 MB of weights and 4.7 MB of cache, and each
 // of the three separate passes is too short to get the memory system up to speed: a cold 16.8 MB
-// stream over the whole chip takes about 6 us.  Here every load of the step is issued at kernel
-// entry, W_UK first, so the W_UK, cache and W_UV streams overlap, and the dependencies between
-// the phases are handed over inside the launch.
+// stream over the whole chip takes about 6 us.  Here the three streams follow each other inside
+// one launch and the phases hand their results to each other between workgroups.  Measured on
+// the part, a CU fetching from HBM under full-chip load delivers only about 40 GB/s (each request
+// waits the loaded latency and few are in flight per CU), so the work before the attention is
+// spread by bytes per CU, not by workgroup count.
 //
 // Grid: 256 workgroups (one per CU; the LDS use forces that), 512 threads.  Waves 0-3 compute;
 // waves 4-7 only move data into LDS and then take part in the workgroup's barriers, so no compute
 // wave ever waits for a prefetch it did not need (s_waitcnt counts a wave's own memory operations
 // in order).  Workgroup r sits on XCD r % 8; slot r / 8:
 //  * slots 0-15: attention workgroup (split s = 4 (r % 8) + slot / 4 of the token tiles, head
-//    block g = slot % 4 of 32 heads); the four head blocks of a split share an XCD, so a tile is
-//    read from HBM once and from that XCD's L2 three times;
+//    block g = slot % 4 of 32 heads); the four head blocks of a split share an XCD and start on
+//    different tiles, so a tile is read from HBM once and from that XCD's L2 three times;
 //  * slots 16-31: projection workgroup for head h = 16 (r % 8) + slot - 16.
-// Phase A (every workgroup, compute wave w): the 16 KB piece of W_UK for head 32 w + r / 8 and
-// latent columns 64 (r % 8) .. + 63; the 64 sums are rounded to bf16 and published.
-// Phase B (attention): the split's (at most four) 32-token tiles were DMA'd into LDS by the loader
+// Phase A: q' is cut into 1024 pieces (head, 64 latent columns), each from a 16 KB block of
+// W_UK; an attention workgroup computes kPA of them (it also fetches 144 KB of tiles), a
+// projection workgroup 8 - kPA.  The sums are rounded to bf16 and published.
+// Phase B (attention): the split's (at most four) 32-token tiles are DMA'd into LDS by the loader
 // waves, one 9 KB column slice per compute wave.  Wave w computes the partial scores of its
 // latent columns 128 w .. + 127 and rope dimensions 16 w .. + 15 (9 MFMA 32x32x16 per tile), the
 // four partials are added through LDS, the softmax of the split is exact (all of its scores are
 // held at once: its maximum, then 2^(s - m)), and wave w multiplies its columns by the
-// probabilities (8 MFMA per tile).  The partial (m, l, acc) per head is published.
-// Phase C (projection): W_UV[h] (128 KB) was DMA'd into LDS at entry; the 32 splits' partials of
-// head h are merged (log-sum-exp) into o_lat[h] and multiplied by W_UV[h].
+// probabilities (8 MFMA per tile).  The partial (m, l, acc / l) per head is published.
+// Phase C (projection): W_UV[h] (128 KB) is DMA'd into LDS after the workgroup's absorb pieces
+// (delayed and paced so that it leaves the fabric to the tiles); the 32 splits' partials of head h
+// are merged (log-sum-exp) into o_lat[h] and multiplied by W_UV[h].
 //
 // Hand-over between workgroups: the producer writes its data with device-coherent stores (sc1),
 // waits for them to complete (s_waitcnt vmcnt(0)), then sets one flag word per consumer (sc1
@@ -54,14 +58,29 @@ constexpr int kPRow = 272;                     // bytes per head row of the prob
 constexpr int kLinvOff = 12288;                // exchange-buffer offset of the 1 / l array
 constexpr unsigned kCoh = 16;                  // buffer cache policy: sc1 (device-coherent)
 constexpr uint64_t kWaitTicks = 2000000;       // 20 ms at the 100 MHz s_memrealtime clock
-#ifndef MLA_STEP_FORM
-#define MLA_STEP_FORM 1
-#endif
 #ifndef MLA_STEP_PACE
-#define MLA_STEP_PACE 8
+#define MLA_STEP_PACE 4
 #endif
-constexpr int kStepForm = MLA_STEP_FORM;       // 1: one launch; 2: absorb kernel + attention kernel
 constexpr int kStepPace = MLA_STEP_PACE;       // s_sleep between the W_UV loads of a loader wave
+#ifndef MLA_STEP_WUV_DELAY
+#define MLA_STEP_WUV_DELAY 600
+#endif
+constexpr int kWuvDelay = MLA_STEP_WUV_DELAY;  // W_UV loads start this many 10 ns ticks after the workgroup
+#ifndef MLA_STEP_STAGGER
+#define MLA_STEP_STAGGER 1
+#endif
+constexpr bool kStagger = MLA_STEP_STAGGER != 0;  // head blocks of a split start on different tiles
+#ifndef MLA_STEP_PA
+#define MLA_STEP_PA 2
+#endif
+#ifndef MLA_STEP_TILES_AFTER_ABSORB
+#define MLA_STEP_TILES_AFTER_ABSORB 1
+#endif
+// The absorb phase is cut into 1024 pieces (head, block of 64 latent columns); each attention
+// workgroup takes kPA of them (one per compute wave), each projection workgroup 8 - kPA.
+constexpr int kPA = MLA_STEP_PA;
+constexpr bool kTilesAfterAbsorb = MLA_STEP_TILES_AFTER_ABSORB != 0;   // attention tiles after its pieces
+static_assert(kPA >= 0 && kPA <= 4, "one piece per attention compute wave at most");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
@@ -159,23 +178,38 @@ __device__ __forceinline__ void issue_tile(const StepArgs& a, int t, int len, in
   lds_dma16(rbase, roff, st + kSRope);
 }
 
-// Phase A, compute wave `wave` of workgroup r: q'[hw][c0 .. c0 + 63] with hw = 32 wave + r / 8 and
-// c0 = 64 (r % 8) (the 16 KB piece of W_UK[hw]); lane (rg, cc) sums rows 16 rg .. 16 rg + 15 of
-// columns c0 + 8 cc .. + 7.  xq: 256 bytes of LDS private to the wave.  `publish`: the one-launch
-// form, which hands the piece to the attention workgroups through flags.
-__device__ __forceinline__ void absorb_piece(const StepArgs& a, int r, int wave, int lane, uint8_t* xq, bool publish) {
-  {
-    const int hw = 32 * wave + (r >> 3);
-    const int c0 = (r & 7) * 64;
-    const int rg = lane >> 3, cc = lane & 7;
-    u32x4 qv = {0u, 0u, 0u, 0u};
-    if (lane < 16) qv = *(const u32x4*)(a.q_C + hw * 128 + lane * 8);
-    u32x4 wv[16];
+// Phase A, one compute wave: pieces q0 .. q0 + NP - 1 of q', piece q = q'[hw][c0 .. c0 + 63] with
+// hw = q / 8 and c0 = 64 (q % 8), from the 16 KB block of W_UK[hw] under those columns (all loads
+// issued before any arithmetic).  Lane (rg, cc) sums rows 16 rg .. 16 rg + 15 of columns
+// c0 + 8 cc .. + 7.  xq: NP * 256 bytes of LDS private to the wave.  The pieces are written with
+// device-coherent stores, which complete before one flag per piece and consumer is set: compute
+// wave (q % 8) / 2 of each of the 32 attention workgroups of head block hw / 32 (lane = split),
+// flag index 2 (hw % 32) + q % 2 among that wave's 64 pieces.
+template <int NP>
+__device__ __forceinline__ void absorb_pieces(const StepArgs& a, int q0, int lane, uint8_t* xq) {
+  const int rg = lane >> 3, cc = lane & 7;
+  u32x4 qv[NP];
+  u32x4 wv[NP][16];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    const int hw = (q0 + e) >> 3;
+    qv[e] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 16) qv[e] = *(const u32x4*)(a.q_C + hw * 128 + lane * 8);
+  }
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    const int hw = (q0 + e) >> 3, c0 = ((q0 + e) & 7) * 64;
     const uint16_t* wp = a.W_UK + ((int64_t)hw * 128 + 16 * rg) * 512 + c0 + cc * 8;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) wv[k] = *(const u32x4*)(wp + k * 512);
-    if (lane < 16) *(u32x4*)(xq + lane * 16) = qv;
-    const u32x4 qa = *(const u32x4*)(xq + 32 * rg), qb = *(const u32x4*)(xq + 32 * rg + 16);
+    for (int k = 0; k < 16; ++k) wv[e][k] = *(const u32x4*)(wp + k * 512);
+  }
+#pragma unroll
+  for (int e = 0; e < NP; ++e)
+    if (lane < 16) *(u32x4*)(xq + e * 256 + lane * 16) = qv[e];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    const int hw = (q0 + e) >> 3, c0 = ((q0 + e) & 7) * 64;
+    const u32x4 qa = *(const u32x4*)(xq + e * 256 + 32 * rg), qb = *(const u32x4*)(xq + e * 256 + 32 * rg + 16);
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
@@ -185,60 +219,49 @@ __device__ __forceinline__ void absorb_piece(const StepArgs& a, int r, int wave,
       const float q = (k & 1) ? bf16_hi(qw) : bf16_lo(qw);
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2) {
-        acc[2 * c2] = fmaf(q, bf16_lo(wv[k][c2]), acc[2 * c2]);
-        acc[2 * c2 + 1] = fmaf(q, bf16_hi(wv[k][c2]), acc[2 * c2 + 1]);
+        acc[2 * c2] = fmaf(q, bf16_lo(wv[e][k][c2]), acc[2 * c2]);
+        acc[2 * c2 + 1] = fmaf(q, bf16_hi(wv[e][k][c2]), acc[2 * c2 + 1]);
       }
     }
     // lane (rg, cc) now holds column c0 + 8 cc + rg; lanes with rg even store two columns
     const float s = sum8_over_bits543(acc, lane);
     const float s1 = __shfl_xor(s, 8, 64);
-    if (!publish) {
-      if ((rg & 1) == 0) *(uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg) = pack_bf16x2(s, s1);
-      return;
-    }
-    // one launch: device-coherent store, completed before one flag per consumer is set (compute
-    // wave cw = (r % 8) / 2 of each attention workgroup of head block `wave`, producer index
-    // 2 (r / 8) + r % 2 among its 64 producers)
     if ((rg & 1) == 0)
       __hip_atomic_store((uint32_t*)(a.qp + hw * 512 + c0 + cc * 8 + rg), pack_bf16x2(s, s1), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    compiler_fence();
-    if (lane < kStepSplits) {
-      const int cw = (r & 7) >> 1, p = 2 * (r >> 3) + (r & 1);
-      coh_store_i32(a.fa + ((wave * kStepSplits + lane) * 4 + cw) * 64 + p, 1);
+  }
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  compiler_fence();
+  if (lane < kStepSplits) {
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      const int q = q0 + e, hw = q >> 3;
+      coh_store_i32(a.fa + (((hw >> 5) * kStepSplits + lane) * 4 + ((q & 7) >> 1)) * 64 + 2 * (hw & 31) + (q & 1), 1);
     }
   }
 }
 
-// Absorb kernel: q'[h] = W_UK[h]^T q_C[h] for all heads, 64 columns of four heads per workgroup
-// (one head per compute wave), and, on the side, the cache tiles that the attention kernel's
-// workgroups on this XCD read first are pulled into this XCD's L2.
-__global__ __launch_bounds__(512) void k_step_absorb(StepArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kSSlice + 1024];
-  const int r = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t* xb = lds + 4 * kSSlice;
-  if (wave >= 4) {
-    // tile (r / 8) / 4 of split 4 (r % 8) + (r / 8) % 4: the attention workgroups of that split
-    // run on this workgroup's XCD (r % 8) in the next kernel
-    const int slot = r >> 3;
-    if (slot >= 16) return;
-    const int split = 4 * (r & 7) + (slot & 3), i = slot >> 2;
-    const int len = max(load_uniform_i32(a.seq_lens), 0);
-    const int T = min(tiles_of(len), kStepSplits * kStepTiles);
-    const int t0 = split * T / kStepSplits, ntl = (split + 1) * T / kStepSplits - t0;
-    if (i < ntl) issue_tile(a, t0 + i, len, wave - 4, lds + (wave - 4) * kSSlice);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+// The pieces of compute wave `wave` of workgroup r: attention workgroups (r < 128) take pieces
+// kPA r + wave for wave < kPA; projection workgroup r - 128 takes the 8 - kPA pieces after
+// 128 kPA + (r - 128) (8 - kPA), spread over its four compute waves.
+__device__ __forceinline__ void absorb_wave(const StepArgs& a, int r, int wave, int lane, uint8_t* xq) {
+  if (r < 128) {
+    if (wave < kPA) absorb_pieces<1>(a, kPA * r + wave, lane, xq);
     return;
   }
-  absorb_piece(a, r, wave, lane, xb + wave * 256, false);
+  constexpr int n = 8 - kPA;
+  const int base = 128 * kPA + (r - 128) * n;
+  const int cnt = n / 4 + (wave < n % 4 ? 1 : 0);
+  const int q0 = base + wave * (n / 4) + min(wave, n % 4);
+  if (cnt == 2) {
+    absorb_pieces<2>(a, q0, lane, xq);
+  } else if (cnt == 1) {
+    absorb_pieces<1>(a, q0, lane, xq);
+  }
 }
 
-template <bool ONE, int PACE>
-__global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
+__global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -249,6 +272,7 @@ __global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
   const int g = slot & 3;
   const int hproj = 16 * xcd + slot - 16;
   uint8_t* xb = lds + kRingBytes;
+  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
 
   // tile range of this split (attention): T tiles of the sequence cut evenly over kStepSplits
   auto tile_range = [&](int len, int& t0, int& ntl) __attribute__((always_inline)) {
@@ -262,20 +286,29 @@ __global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
     const int lw = wave - 4;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    if (ONE) lds_barrier();   // B0: the compute waves have published their q' pieces
+    // B0: the compute waves have published their q' pieces (workgroups that absorb)
+    if (!attn || (kPA > 0 && kTilesAfterAbsorb)) lds_barrier();
     if (attn) {
       const int len = max(load_uniform_i32(a.seq_lens), 0);
       int t0, ntl;
       tile_range(len, t0, ntl);
-      for (int i = 0; i < ntl; ++i) issue_tile(a, t0 + i, len, lw, lds + (i * 4 + lw) * kSSlice);
+      // the four head blocks of a split start on different tiles, so that only the first request for
+      // a tile waits for HBM and the others find it in (or on its way into) the XCD's L2
+      for (int k = 0; k < ntl; ++k) {
+        const int i = kStagger ? (k + g) % ntl : k;
+        issue_tile(a, t0 + i, len, lw, lds + (i * 4 + lw) * kSSlice);
+      }
+      if (kPA > 0 && !kTilesAfterAbsorb) lds_barrier();   // B0
     } else {
       // W_UV[h]: row i (1 KB) at LDS i * 1024, 16-byte chunk c at position c ^ (i & 63)
       const uint8_t* wbase = (const uint8_t*)a.W_UV + (int64_t)hproj * 128 * 1024;
+      if (kWuvDelay > 0)
+        while (__builtin_amdgcn_s_memrealtime() - t_entry < (uint64_t)kWuvDelay) __builtin_amdgcn_s_sleep(4);
       for (int k = 0; k < 32; ++k) {
         const int i = 32 * lw + k;
         lds_dma16(wbase + i * 1024, 16u * (uint32_t)(ln ^ (i & 63)),
                   __builtin_amdgcn_readfirstlane(lds_addr(lds + i * 1024)));
-        if (PACE > 0) __builtin_amdgcn_s_sleep(PACE);
+        if (kStepPace > 0) __builtin_amdgcn_s_sleep(kStepPace);
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -293,8 +326,8 @@ __global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
     return;
   }
 
-  if (ONE) {
-    absorb_piece(a, r, wave, lane, xb + wave * 256, true);
+  if (!attn || kPA > 0) {
+    absorb_wave(a, r, wave, lane, xb + wave * 512);
     lds_barrier();   // B0
   }
   const int len = max(load_uniform_i32(a.seq_lens), 0);
@@ -305,8 +338,8 @@ __global__ __launch_bounds__(512) void k_step_attend(StepArgs a) {
     int t0, ntl;
     tile_range(len, t0, ntl);
     // this wave's folded-query slice: latent k-steps 8 cw .. 8 cw + 7 (qf[0..7]) and rope k-step cw
-    // (one launch: after the flags of its 64 producers)
-    if (ONE) wait_flags(a.fa + ((g * kStepSplits + split) * 4 + cw) * 64, lane, 64, a.err);
+    // after the flags of its producers
+    wait_flags(a.fa + ((g * kStepSplits + split) * 4 + cw) * 64, lane, 64, a.err);
     const __amdgpu_buffer_rsrc_t qr = rsrc(a.qp);
     u32x4 qf[9];
 #pragma unroll
@@ -586,14 +619,7 @@ __global__ void k_step_zero(int* p, int64_t n) {
 }
 
 hipError_t launch_step_b1(const StepArgs& a, hipStream_t s) {
-  if (kStepForm == 1) {
-    hipLaunchKernelGGL((k_step_attend<true, kStepPace>), dim3(kStepWGs), dim3(512), 0, s, a);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(k_step_absorb, dim3(kStepWGs), dim3(512), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_step_attend<false, kStepPace>), dim3(kStepWGs), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(k_step_b1, dim3(kStepWGs), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
