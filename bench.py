@@ -141,7 +141,8 @@ def parse():
                     help="decode row: one GPU's share of the workload split by token range over G GPUs "
                          "(every sequence keeps 1/G of its tokens); the exchange between GPUs is not run")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
-                    help="only run 4 plain device copies of MB megabytes (a reference for HBM byte counters)")
+                    help="only run 4 plain device copies and 4 read-only sums of MB megabytes (a reference for "
+                         "HBM byte counters and the streaming ceiling)")
     return ap.parse_args()
 
 
@@ -236,8 +237,21 @@ def main():
         cb.record()
         cb.synchronize()
         ms = ca.elapsed_time(cb) / 4
+        # read-only stream: a float sum over the same bytes (the reduction writes one word)
+        fv = src.view(torch.float32)
+        _ = fv.sum()
+        torch.cuda.synchronize()
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ra.record()
+        for _ in range(4):
+            _ = fv.sum()
+        rb.record()
+        rb.synchronize()
+        rms = ra.elapsed_time(rb) / 4
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5, "copy_ms": round(ms, 4),
-                          "read_plus_write_TBps": round(2 * n / (ms * 1e-3) / 1e12, 3)}), flush=True)
+                          "read_plus_write_TBps": round(2 * n / (ms * 1e-3) / 1e12, 3),
+                          "sums": 5, "sum_ms": round(rms, 4), "read_only_TBps": round(n / (rms * 1e-3) / 1e12, 3)}),
+              flush=True)
         return
 
     if args.row == "append":

@@ -5,6 +5,15 @@
                                  --out profiles/<kernel>_<workload>_kernel_stats.txt
   python bench_profiles.py pmc --kernel k_partial_mfma --workload v3-b1 --fetch <csv> --write <csv>
                                --cal-fetch <csv> --cal-write <csv> --cal-bytes N --cmd "<commands>"
+  python bench_profiles.py sq --kernel k_partial_mfma --workload v3-b64-var --csv <csv> [<csv> ...]
+                              --cmd "<commands>" [--tiles-per-wg T]
+  python bench_profiles.py ceiling --csv <kernel_stats.csv> --trace <kernel_trace.csv> --bench <stdout>
+                                   --cmd "<command>" --out profiles/<name>.txt
+
+The sq form averages per dispatch every SQ / GRBM counter (and the derived MfmaUtil) found for one
+kernel in the given counter runs and writes profiles/<kernel>_<workload>_sq.txt: instructions per
+wave by class and the MFMA busy share.  The ceiling form summarises a --copy-calibration run: the
+copy and read-only reduction kernels and their bandwidths.
 
 The pmc form reads per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of one kernel from two separate
 counter runs, scales each by what the same counter reads for a plain device copy of known size
@@ -140,6 +149,61 @@ def cmd_pmc(a):
     print("\n".join(txt))
 
 
+def cmd_sq(a):
+    vals = {}   # counter -> {dispatch: value}
+    for path in a.csv:
+        for r in _rows(path):
+            if a.kernel not in _col(r, "Kernel_Name", "kernel_name"):
+                continue
+            c = _col(r, "Counter_Name", "counter_name")
+            d = (path, _col(r, "Dispatch_Id", "dispatch_id"))
+            vals.setdefault(c, {}).setdefault(d, 0.0)
+            vals[c][d] += float(_col(r, "Counter_Value", "counter_value"))
+    if not vals:
+        raise SystemExit(f"no counter rows for kernels matching {a.kernel!r}")
+    mean = {c: statistics.mean(v.values()) for c, v in vals.items()}
+    n = {c: len(v) for c, v in vals.items()}
+    waves = mean.get("SQ_WAVES")
+    txt = [f"# rocprofv3 SQ counters: {a.kernel} on {a.workload}", "", "Commands:", ""]
+    txt += ["    " + c for c in a.cmd.split(" ;; ")]
+    txt += ["", "| counter | per dispatch | per wave | dispatches |", "|---|---|---|---|"]
+    for c in sorted(mean):
+        pw = f"{mean[c] / waves:.1f}" if waves and c.startswith("SQ_INSTS") else ""
+        txt.append(f"| {c} | {mean[c]:.6g} | {pw} | {n[c]} |")
+    if waves and a.tiles_per_wg:
+        txt += ["", f"Per 32-token tile and wave ({a.tiles_per_wg} tiles per workgroup):"]
+        for c in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+            if c in mean:
+                txt.append(f"    {c}: {mean[c] / waves / a.tiles_per_wg:.1f}")
+    if "MfmaUtil" in mean:
+        txt += ["", f"MFMA busy (MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs): "
+                    f"{mean['MfmaUtil']:.2f} %"]
+    out = os.path.join(ROOT, "profiles", f"{a.kernel}_{a.workload}_sq.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
+
+
+def cmd_ceiling(a):
+    rows = _rows(a.csv)
+    meas = None
+    with open(a.bench) as f:
+        for line in f:
+            if line.startswith("{") and "copy_calibration_bytes" in line:
+                meas = json.loads(line)
+    txt = [f"# HBM streaming ceiling on this part: plain device copy and read-only reduction", "", "Command:", "",
+           "    " + a.cmd, "", "| kernel | calls | avg us | min us |", "|---|---|---|---|"]
+    for r in rows:
+        name = _col(r, "Name", "KernelName", "Kernel_Name").split("(")[0].replace("void ", "")
+        txt.append(f"| {name[:90]} | {_col(r, 'Calls')} | {float(_col(r, 'AverageNs')) / 1e3:.2f} | "
+                   f"{float(_col(r, 'MinNs')) / 1e3:.2f} |")
+    if meas:
+        txt += ["", "HIP-event measurement of the same run: " + json.dumps(meas)]
+    with open(a.out, "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -162,8 +226,19 @@ def main():
     p.add_argument("--cal-bytes", type=int, required=True)
     p.add_argument("--cal-kernel", default="copy")
     p.add_argument("--cmd", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--workload", required=True)
+    q.add_argument("--csv", nargs="+", required=True)
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--tiles-per-wg", type=float, default=0.0)
+    c = sub.add_parser("ceiling")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--bench", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    cmd_stats(a) if a.what == "stats" else cmd_pmc(a)
+    {"stats": cmd_stats, "pmc": cmd_pmc, "sq": cmd_sq, "ceiling": cmd_ceiling}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -164,9 +164,12 @@ void k_partial_mfma(PartialArgs a) {
     const int last = ts.last;
     if (k < kLatJobs) {
       if (!FP8) {
+        // row r = wave + NWAVE k; since wave < NWAVE and NWAVE divides 8, bit 3 of r is bit 3 of
+        // NWAVE k: the swizzle choice is a constant of the unrolled job
+        // the row offset goes into the scalar base: the lane offset is then loop-invariant
         const int r = wave + NWAVE * k;
         const uint32_t roff = (uint32_t)min(r, last) * lstride;
-        lds_dma16(ts.lbase, (((r >> 3) & 1) ? vx1 : vx0) + roff, ts.st + r * kLatStride);
+        lds_dma16(ts.lbase + roff, (((NWAVE * k) >> 3) & 1) ? vx1 : vx0, ts.st + r * kLatStride);
       } else {
         const int pr = wave + NWAVE * k;       // row pair
         const uint32_t r0 = (uint32_t)min(2 * pr, last) * lstride;
@@ -194,7 +197,7 @@ void k_partial_mfma(PartialArgs a) {
     // held in registers across the tile loop
     asm volatile("" : "+s"(ts.lbase), "+s"(ts.rbase), "+s"(ts.sbase), "+s"(ts.st), "+s"(ts.last));
     uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
-    asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+    if constexpr (FP8) asm volatile("" : "+v"(vf0), "+v"(vf1));
 #pragma unroll
     for (int k = 0; k < LPT; ++k) job(ts, k, vx0, vx1, vf0, vf1);
   };  auto issue = [&](int it) __attribute__((always_inline)) { issue_src(prep(it)); };
@@ -290,7 +293,7 @@ void k_partial_mfma(PartialArgs a) {
         const int k0 = (s / 2) * LPT / 16, k1 = (s / 2 + 1) * LPT / 16;   // constants after unrolling
         if (k0 < k1) {
           uint32_t vx0 = voff_x0, vx1 = voff_x1, vf0 = voff_f8_0, vf1 = voff_f8_1;
-          asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(vf0), "+v"(vf1));
+          if constexpr (FP8) asm volatile("" : "+v"(vf0), "+v"(vf1));
 #pragma unroll
           for (int k = k0; k < k1; ++k) job(js, k, vx0, vx1, vf0, vf1);
         }
@@ -440,8 +443,12 @@ void k_partial_mfma(PartialArgs a) {
         }
       }
     }
+  };
+  // the output accumulator lives in AGPRs (pinned after the softmax that follows each value step,
+  // which leaves the scheduler free to place the softmax between the value MFMAs)
+  auto pin_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));  // the output accumulator lives in AGPRs
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[i]));
   };
 
   // ---------------------------------------------------------------- pipeline
@@ -529,6 +536,7 @@ void k_partial_mfma(PartialArgs a) {
       if constexpr (!FP8) rescale_with(fl, (it - 1) & 1);
       value(stage(it - 1), (it - 1) & 1);
       softmax(S, nvalid, stage(it), it & 1);
+      pin_acc();
     }
     // the workgroup's last tile, if it is in this segment (nothing left to load)
     if (it < it_end) {
@@ -539,6 +547,7 @@ void k_partial_mfma(PartialArgs a) {
       const f32x16 S = score(stage(it), std::false_type{}, nsrc);
       value(stage(it - 1), (it - 1) & 1);
       softmax(S, nvalid, stage(it), it & 1);
+      pin_acc();
       ++it;
     }
     // value of the segment's last tile (its probabilities are published by this barrier)
@@ -546,6 +555,7 @@ void k_partial_mfma(PartialArgs a) {
     lds_barrier();
     rescale((it - 1) & 1);
     value(stage(it - 1), (it - 1) & 1);
+    pin_acc();
 
     // ------------------------------------------------------------ segment partial -> slot w + b
     {
