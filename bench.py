@@ -294,7 +294,8 @@ def main():
     W = args.num_splits or ops.mla_decode_auto_splits(wl.B, wl.H, wl.n_max)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
-    print(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB, splits={W}", file=sys.stderr, flush=True)
+    form = "one launch" if one_launch_step(wl, args.num_splits) else f"three or four calls, {W} splits"
+    print(f"[bench] {R} input copies of {per_copy / 1e6:.1f} MB, {form}", file=sys.stderr, flush=True)
 
     def one(i):
         c = copies[i % R]
