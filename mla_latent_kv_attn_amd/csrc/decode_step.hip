@@ -29,8 +29,9 @@
 // waves, one 9 KB column slice per compute wave.  Wave w computes the partial scores of its
 // latent columns 128 w .. + 127 and rope dimensions 16 w .. + 15 (9 MFMA 32x32x16 per tile), the
 // four partials are added through LDS, the softmax of the split is exact (all of its scores are
-// held at once: its maximum, then 2^(s - m)), and wave w multiplies its columns by the
-// probabilities (8 MFMA per tile).  The partial (m, l, acc / l) per head is published.
+// held at once: its maximum, then 2^(s - m)); compute wave w and loader wave 4 + w each multiply
+// half of slice w's columns by the probabilities (4 MFMA per tile each).  The partial
+// (m, l, acc / l) per head is published.
 // Phase C (projection): W_UV[h] (128 KB) is DMA'd into LDS after the workgroup's absorb pieces
 // (delayed and paced so that it leaves the fabric to the tiles); the 32 splits' partials of head h
 // are merged (log-sum-exp) into o_lat[h] and multiplied by W_UV[h].
@@ -261,6 +262,82 @@ __device__ __forceinline__ void absorb_wave(const StepArgs& a, int r, int wave, 
   }
 }
 
+// Value product of one wave over the split's tiles for latent column blocks cb0 and cb0 + 1 of
+// slice cw (columns 128 cw + 32 cb .. + 31): acc[k] = O^T block (32 columns x 32 heads) of block
+// cb0 + k.  Step 2 i + ks takes tokens 16 ks .. 16 ks + 15 of tile i, its operands read one step
+// ahead (the probabilities from the head rows in xb, the latent operand through transposing LDS
+// reads).
+__device__ __forceinline__ void value_blocks(const uint8_t* lds, const uint8_t* xb, int cw, int cb0, int ntl, int lane,
+                                             f32x16 (&acc)[2]) {
+  const int hl = lane & 31, hf = lane >> 5;
+  const int G = lane >> 4;
+  const int vrow0 = 8 * (G >> 1) + ((lane & 15) >> 2);
+  auto v_ops = [&](int stp, u32x4 (&av)[2], u32x4& pv) __attribute__((always_inline)) {
+    const int i = min(stp >> 1, kStepTiles - 1), ks = stp & 1;
+    const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
+    pv = *(const u32x4*)(xb + hl * kPRow + 2 * (kTile * i + 16 * ks + 8 * hf));
+    const int R = 16 * ks + vrow0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int cch = 4 * (cb0 + k) + 2 * (G & 1) + ((lane & 3) >> 1);
+      const uint8_t* pa = st + R * 256 + 16 * (cch ^ (R & 15)) + 8 * (lane & 1);
+      const uint8_t* pb = st + (R + 4) * 256 + 16 * (cch ^ ((R + 4) & 15)) + 8 * (lane & 1);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pb));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      av[k] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+  };
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+  u32x4 ca[2], na[2], cp, np;
+  v_ops(0, ca, cp);
+#pragma unroll
+  for (int stp = 0; stp < 2 * kStepTiles; ++stp) {
+    if (stp + 1 < 2 * kStepTiles) v_ops(stp + 1, na, np);
+    if ((stp >> 1) < ntl) {
+      acc[0] = mfma32x32x16(ca[0], cp, acc[0]);
+      acc[1] = mfma32x32x16(ca[1], cp, acc[1]);
+    }
+    ca[0] = na[0];
+    ca[1] = na[1];
+    cp = np;
+  }
+}
+
+// The split's mean acc / l of blocks cb0, cb0 + 1 of slice cw as bf16 rows of the workspace: each
+// 32 x 32 block is turned into head rows of 64 bytes through the LDS of tile 0's slice cw (free
+// once every wave has passed the barrier after the value products; 16-byte chunk c of row n at
+// position c ^ (n & 3)), then stored as 16-byte pieces of whole rows (a store of pieces scattered
+// over 32 rows per lane pair issues far more slowly).
+__device__ __forceinline__ void store_blocks(const StepArgs& a, uint8_t* lds, const uint8_t* xb, int cw, int cb0,
+                                             int split, int g, int lane, const f32x16 (&acc)[2]) {
+  const int hl = lane & 31, hf = lane >> 5;
+  const float* linv = (const float*)(xb + kLinvOff);
+  const float li = linv[hl];
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  uint8_t* tb = lds + cw * kSSlice;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4)
+      *(u32x2*)(tb + (cb0 + k) * 2048 + hl * 64 + 16 * (v4 ^ (hl & 3)) + 8 * hf) =
+          u32x2{pack_bf16x2(acc[k][4 * v4] * li, acc[k][4 * v4 + 1] * li),
+                pack_bf16x2(acc[k][4 * v4 + 2] * li, acc[k][4 * v4 + 3] * li)};
+  const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
+  const int tc = ln & 3;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const int cb = cb0 + k;
+      const int row = (ln >> 2) + 16 * ps;
+      const u32x4 v = *(const u32x4*)(tb + cb * 2048 + row * 64 + 16 * (tc ^ (row & 3)));
+      coh_store4(pr, (uint32_t)(((split * 128 + 32 * g + row) * 512 + 128 * cw + 32 * cb + 8 * tc) * 2), v);
+    }
+}
+
 __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const int r = blockIdx.x;
@@ -313,16 +390,24 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();   // B1: the prefetched data is in LDS
-    // then the barriers the compute waves take after B1 (attention: two per tile, the
-    // probabilities, the published partials; projection: three), so that every barrier of the
-    // workgroup sees all eight waves
-    int nb = 3;
-    if (attn) {
-      int t0, ntl;
-      tile_range(max(load_uniform_i32(a.seq_lens), 0), t0, ntl);
-      nb = 2 + 2 * ntl;
+    // then the barriers the compute waves take after B1, so that every barrier of the workgroup
+    // sees all eight waves: projection, three; attention, two per tile and the probabilities,
+    // then this wave's half of the value product (V), its mean rows, and the published partials
+    if (!attn) {
+      for (int k = 0; k < 3; ++k) lds_barrier();
+      return;
     }
-    for (int k = 0; k < nb; ++k) lds_barrier();
+    int t0, ntl;
+    tile_range(max(load_uniform_i32(a.seq_lens), 0), t0, ntl);
+    for (int k = 0; k < 2 * ntl + 1; ++k) lds_barrier();
+    f32x16 acc[2];
+    if (ntl > 0) value_blocks(lds, xb, lw, 2, ntl, lane, acc);
+    lds_barrier();   // V
+    if (ntl > 0) store_blocks(a, lds, xb, lw, 2, split, g, lane, acc);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compiler_fence();
+    lds_barrier();   // the partial stores of every wave have completed
     return;
   }
 
@@ -431,70 +516,13 @@ __global__ __launch_bounds__(512) void k_step_b1(StepArgs a) {
     if (sc == 0) linv[sn] = l > 0.f ? 1.f / l : 0.f;
     lds_barrier();   // the probabilities and 1 / l of all 32 heads are in LDS
 
-    // value: acc[cb] = O^T block (latent columns 128 cw + 32 cb .. + 31) x (32 heads); step
-    // 2 i + ks takes tokens 16 ks .. 16 ks + 15 of tile i, its operands read one step ahead
-    if (ntl > 0) {
-      const int G = lane >> 4;
-      const int vrow0 = 8 * (G >> 1) + ((lane & 15) >> 2);
-      auto v_ops = [&](int stp, u32x4 (&av)[4], u32x4& pv) __attribute__((always_inline)) {
-        const int i = min(stp >> 1, kStepTiles - 1), ks = stp & 1;
-        const uint8_t* st = lds + (i * 4 + cw) * kSSlice;
-        pv = *(const u32x4*)(xb + hl * kPRow + 2 * (kTile * i + 16 * ks + 8 * hf));
-        const int R = 16 * ks + vrow0;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int cch = 4 * cb + 2 * (G & 1) + ((lane & 3) >> 1);
-          const uint8_t* pa = st + R * 256 + 16 * (cch ^ (R & 15)) + 8 * (lane & 1);
-          const uint8_t* pb = st + (R + 4) * 256 + 16 * (cch ^ ((R + 4) & 15)) + 8 * (lane & 1);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pb));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          av[cb] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-        }
-      };
-      f32x16 acc[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
-      u32x4 ca[4], na[4], cp, np;
-      v_ops(0, ca, cp);
-#pragma unroll
-      for (int stp = 0; stp < 2 * kStepTiles; ++stp) {
-        if (stp + 1 < 2 * kStepTiles) v_ops(stp + 1, na, np);
-        if ((stp >> 1) < ntl) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[cb] = mfma32x32x16(ca[cb], cp, acc[cb]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) ca[cb] = na[cb];
-        cp = np;
-      }
-      // partial rows to the workspace as bf16 acc / l (the split's softmax-weighted latent mean):
-      // each 32 x 32 block is turned into head rows of 64 bytes through this wave's own ring
-      // slice (no other wave reads it; 16-byte chunk c of row n at position c ^ (n & 3)), then
-      // stored as 16-byte pieces of whole rows (a store of pieces scattered over 32 rows per
-      // lane pair issues far more slowly)
-      const float li = linv[hl];
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      uint8_t* tb = lds + cw * kSSlice;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4)
-          *(u32x2*)(tb + cb * 2048 + hl * 64 + 16 * (v4 ^ (hl & 3)) + 8 * hf) =
-              u32x2{pack_bf16x2(acc[cb][4 * v4] * li, acc[cb][4 * v4 + 1] * li),
-                    pack_bf16x2(acc[cb][4 * v4 + 2] * li, acc[cb][4 * v4 + 3] * li)};
-      const __amdgpu_buffer_rsrc_t pr = rsrc(a.part_acc);
-      const int tc = ln & 3;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {
-          const int row = (ln >> 2) + 16 * ps;
-          const u32x4 v = *(const u32x4*)(tb + cb * 2048 + row * 64 + 16 * (tc ^ (row & 3)));
-          coh_store4(pr, (uint32_t)(((split * 128 + 32 * g + row) * 512 + 128 * cw + 32 * cb + 8 * tc) * 2), v);
-        }
-    }
+    // value: compute wave cw takes latent column blocks 0, 1 of its slice, loader wave 4 + cw
+    // blocks 2, 3; then, once no wave reads the tiles any more, both turn their blocks into the
+    // split's mean rows
+    f32x16 acc[2];
+    if (ntl > 0) value_blocks(lds, xb, cw, 0, ntl, lane, acc);
+    lds_barrier();   // V: the value products are done; the tile slices are free
+    if (ntl > 0) store_blocks(a, lds, xb, cw, 0, split, g, lane, acc);
     if (sc == 0)
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m), __float_as_uint(l)}, rsrc(a.part_ml),
                                             (int)((split * 128 + 32 * g + sn) * 8), 0, kCoh);
