@@ -130,7 +130,10 @@ int mla_absorb_q(const void* q_C, const void* W_UK, void* q_abs, int in_dtype, i
  * is the number of partial-pass workgroups over the whole batch (0 = the
  * library's choice for (B, H, max_len), the same choice mla_decode_attn makes).
  * With W workgroups the workspace holds (W + B - 1) partial slots of H x d_c
- * float sums and H (max, sum) pairs, then B + 1 int32 tile prefix sums, then H
+ * float sums (bf16 sums, in the first half of the region, where the large-batch
+ * kernel runs: E4M3 caches, and bf16 caches with B x ceil(max_len / 32) above
+ * 1024 or B above 256) and H (max, sum) pairs, then B + 1 int32
+ * tile prefix sums and one int32 naming the sums' element type, then H
  * int32 counters and min(B, 4) x H x 4 x 128 floats used by the one-kernel form
  * of mla_decode_combine_uv; each of the five regions is rounded up to a multiple
  * of 256 bytes.  Returns 0 for invalid sizes.

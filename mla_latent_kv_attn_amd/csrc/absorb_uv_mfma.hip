@@ -291,9 +291,9 @@ __global__ __launch_bounds__(256) void k_uv_gemv(const float* __restrict__ o_lat
 //      and the last workgroup resets it.  The summation order is fixed, so the result does not
 //      depend on which workgroup finishes last.
 // ---------------------------------------------------------------------------------------------
-template <int NB>
-__global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_t* __restrict__ w,
-                                                    float* __restrict__ out) {
+template <int NB, bool BF>
+__device__ __forceinline__ void combine_uv(const CombineArgs& a, const uint16_t* __restrict__ w,
+                                           float* __restrict__ out) {
   constexpr int kW = 1024;   // segment weights kept in LDS
   __shared__ __attribute__((aligned(16))) float olq[NB][128];
   __shared__ float4 part[7][32];
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
     const int w1 = empty ? -1 : (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
     const int nseg = w1 - w0 + 1;
     const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml[s H]
-    const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + h) * 512 + 128 * q + 4 * c4;   // + s H 512
+    const int64_t src = ((int64_t)(w0 + b) * H + h) * 512 + 128 * q + 4 * c4;   // element + s H 512
     const float2 q0 = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
     // the first 64 segments (8 per thread), all loads in flight together: segments past nseg read
     // the last one (weight 0 below), where a conditional or looped load would be waited on before
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
       const int su = min(sg + 8 * u, max(nseg - 1, 0));
-      x[u] = *(const float4*)(src + su * sstride);
+      x[u] = load_part4<BF>(a.ws_acc, src + su * sstride);
     }
     if (b == 0) {
       const uint16_t* wp = w + ((int64_t)h * 128 + (tid >> 1)) * 512 + 128 * q + 64 * (tid & 1);
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
       o.w = fmaf(f, x[u].w, o.w);
     }
     for (int s = sg + 8 * kPre; s < nseg; s += 8) {
-      const float4 xs = *(const float4*)(src + s * sstride);
+      const float4 xs = load_part4<BF>(a.ws_acc, src + s * sstride);
       const float f = s < kW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M);
       o.x = fmaf(f, xs.x, o.x);
       o.y = fmaf(f, xs.y, o.y);
@@ -446,6 +446,16 @@ __global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_
     }
   }
   if (tid == 0) __hip_atomic_store(a.ws_cnt + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the partial sums are float or bf16, as the partial pass recorded after the tile prefix sums
+template <int NB>
+__global__ __launch_bounds__(256) void k_combine_uv(CombineArgs a, const uint16_t* __restrict__ w,
+                                                    float* __restrict__ out) {
+  if (a.ws_prefix[a.B + 1] == kPartBF16)
+    combine_uv<NB, true>(a, w, out);
+  else
+    combine_uv<NB, false>(a, w, out);
 }
 
 hipError_t launch_combine_uv(const CombineArgs& a, const void* w, float* out, hipStream_t s) {

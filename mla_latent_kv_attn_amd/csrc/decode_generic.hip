@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void k_partial_f32(PartialArgs a) {
   build_tile_prefix(a.seq_lens, a.B, P, L);
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];
+    if (threadIdx.x == 0) a.ws_prefix[a.B + 1] = kPartF32;
     for (int i = threadIdx.x; i < a.H; i += blockDim.x) a.ws_cnt[i] = 0;
   }
   const int NT = P[a.B];
@@ -144,7 +145,8 @@ hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  o = sum_s 2^(m_s - M) acc_s / L,
 //   lse = (M + log2 L) * ln 2       (natural log).   No segment -> o = 0, lse = -inf.
 // The segments of sequence b are the partial-pass workgroups w0..w1 whose tile ranges meet b's
-// tiles (tile prefix sums left in the workspace by the partial pass).
+// tiles (tile prefix sums left in the workspace by the partial pass, followed by the element
+// type of its sums, float or bf16).
 // Grid (H, B, d_c / 128), 256 threads: the workgroup merges 128 columns.  The (m, l) pairs are
 // reduced by the whole workgroup and the segment weights 2^(m_s - M) kept in LDS (the first
 // kCombW of them); thread t then takes float4 column group t % 32 and segments t / 32 + 8 i,
@@ -165,10 +167,8 @@ __device__ __forceinline__ float block_reduce256(float v, bool is_max, float* re
   return v;
 }
 
-__global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
-  __shared__ float4 red[8][33];
-  __shared__ float wts[kCombW];
-  __shared__ float rr[4];
+template <bool BF>
+__device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)[33], float* wts, float* rr) {
   const int h = blockIdx.x, b = blockIdx.y, cq = blockIdx.z, tid = threadIdx.x;
   const int d_c = a.d_c, H = a.H;
   const int c4 = tid & 31, sg = tid >> 5;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (col < d_c) {
-    const float* acc0 = a.ws_acc + ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at acc0 + H d_c s
+    const int64_t e0 = ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at element e0 + H d_c s
     const int64_t astride = (int64_t)H * d_c;
     // four segments per pass, all four loads in flight together; in the last pass segments past
     // nseg read the last one and get weight 0 (a load per remaining segment would be waited on
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
     for (int s = sg; s < nseg; s += 32) {
       float4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(acc0 + min(s + 8 * u, nseg - 1) * astride);
+      for (int u = 0; u < 4; ++u) v[u] = load_part4<BF>(a.ws_acc, e0 + min(s + 8 * u, nseg - 1) * astride);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float f = s + 8 * u < nseg ? weight(s + 8 * u) : 0.f;
@@ -238,6 +238,16 @@ __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
   if (a.lse && tid == 0 && cq == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
 }
 
+__global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
+  __shared__ float4 red[8][33];
+  __shared__ float wts[kCombW];
+  __shared__ float rr[4];
+  if (a.ws_prefix[a.B + 1] == kPartBF16)
+    combine_rows<true>(a, red, wts, rr);
+  else
+    combine_rows<false>(a, red, wts, rr);
+}
+
 constexpr int kCombWB = 128;   // segments whose weights are kept in LDS (the rest are recomputed)
 
 // Combine for batches wide enough to fill the chip with one workgroup per (32-head block,
@@ -245,11 +255,10 @@ constexpr int kCombWB = 128;   // segments whose weights are kept in LDS (the re
 // block's 32 partial rows are 64 KiB contiguous per segment, which thread t reads as float4
 // t + 256 i (i = 0..15: head 2i + t / 128, columns 4 (t % 128) ..), sixteen loads in flight.
 // d_c must be 512.
-__global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
+template <bool BF>
+__device__ __forceinline__ void combine_heads(const CombineArgs& a, float (*red)[32], float* Ms, float* Lsum,
+                                              float (*wts)[32]) {
   constexpr int NI = 16;
-  __shared__ float red[8][32];
-  __shared__ float Ms[32], Lsum[32];
-  __shared__ float wts[kCombWB][32];
   const int hb = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = a.H, d_c = a.d_c;
   const int hr = tid & 31, g = tid >> 5;                       // (m, l) phase: head hr, group g
@@ -267,12 +276,12 @@ __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
   const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
   const int nseg = w1 - w0 + 1;
   const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + hb * 32) * 2);   // (s, head) at ml[s H + head]
-  const int64_t sstride = (int64_t)H * d_c;   // floats per slot
-  const float* src = a.ws_acc + ((int64_t)(w0 + b) * H + hb * 32) * d_c + 4 * c4;   // + (r0 + 2i) d_c + s sstride
+  const int64_t sstride = (int64_t)H * d_c;   // elements per slot
+  const int64_t src = ((int64_t)(w0 + b) * H + hb * 32) * d_c + 4 * c4;   // element + (r0 + 2i) d_c + s sstride
   // the first segment's rows do not depend on the weights: load them during the (m, l) reduction
   float4 x0[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) x0[i] = *(const float4*)(src + (r0 + 2 * i) * d_c);
+  for (int i = 0; i < NI; ++i) x0[i] = load_part4<BF>(a.ws_acc, src + (r0 + 2 * i) * d_c);
   float mloc = -INFINITY;
   for (int s = g; s < nseg; s += 8) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
   red[g][hr] = mloc;
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
   for (int s = 1; s < nseg; ++s) {
     float4 x[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) x[i] = *(const float4*)(src + s * sstride + (r0 + 2 * i) * d_c);
+    for (int i = 0; i < NI; ++i) x[i] = load_part4<BF>(a.ws_acc, src + s * sstride + (r0 + 2 * i) * d_c);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = r0 + 2 * i;
@@ -330,6 +339,16 @@ __global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
   }
   if (a.lse && tid < 32)
     a.lse[(int64_t)b * H + hb * 32 + tid] = (Ms[tid] + log2f(Lsum[tid])) * 0.69314718055994530942f;
+}
+
+__global__ __launch_bounds__(256) void k_combine_heads(CombineArgs a) {
+  __shared__ float red[8][32];
+  __shared__ float Ms[32], Lsum[32];
+  __shared__ float wts[kCombWB][32];
+  if (a.ws_prefix[a.B + 1] == kPartBF16)
+    combine_heads<true>(a, red, Ms, Lsum, wts);
+  else
+    combine_heads<false>(a, red, Ms, Lsum, wts);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {

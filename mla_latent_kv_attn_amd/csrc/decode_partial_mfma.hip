@@ -74,6 +74,7 @@ void k_partial_mfma(PartialArgs a) {
   build_tile_prefix(a.seq_lens, a.B, P, nullptr);
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];
+    if (threadIdx.x == 0) a.ws_prefix[a.B + 1] = kPartBF16;
     for (int i = threadIdx.x; i < a.H; i += blockDim.x) a.ws_cnt[i] = 0;
   }
   const int NT = P[a.B];
@@ -564,27 +565,33 @@ void k_partial_mfma(PartialArgs a) {
       // loop (where they would occupy registers for the whole tile loop)
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      // Row-major workspace: each 32x32 accumulator block goes through this wave's part of the
-      // (now idle) probability buffers, 144-byte rows, and leaves as 8 full 128-byte row
-      // segments per store instruction.  Every wave has finished reading the probabilities once
-      // it passes this barrier.
+      // Row-major workspace of bf16 sums: each pair of 32x32 accumulator blocks (64 latent
+      // columns of 32 heads) goes through this wave's part of the (now idle) probability buffers,
+      // 144-byte rows, and leaves as 8 full 128-byte row segments per store instruction.  Every
+      // wave has finished reading the probabilities once it passes this barrier.
       __builtin_amdgcn_s_waitcnt(lgkmcnt_imm0());
       lds_barrier();
       uint8_t* tb = &pbuf[0][0] + wave * 5120;
       const int trow = ln >> 3, tchunk = ln & 7;
+      static_assert(CPW % 2 == 0 && 32 * 144 <= 5120, "store staging");
 #pragma unroll
       for (int hb = 0; hb < NWAVE; ++hb) {
-        float* dst = a.ws_acc + ((int64_t)(w + b) * H + h0 + hb * 32 + trow) * 512 + 32 * wave * CPW + 4 * tchunk;
+        uint16_t* dst = (uint16_t*)a.ws_acc + ((int64_t)(w + b) * H + h0 + hb * 32 + trow) * 512 +
+                        32 * wave * CPW + 8 * tchunk;
 #pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-          const f32x16& A = acc[hb * CPW + j];
+        for (int j = 0; j < CPW; j += 2) {
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-            *(f32x4*)(tb + (ln & 31) * 144 + (8 * v4 + 4 * (ln >> 5)) * 4) =
-                f32x4{A[4 * v4], A[4 * v4 + 1], A[4 * v4 + 2], A[4 * v4 + 3]};
+          for (int jj = 0; jj < 2; ++jj) {
+            // lane l holds latent columns 8 v4 + 4 (l >> 5) + 0..3 of block j + jj, head l & 31
+            const f32x16& A = acc[hb * CPW + j + jj];
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+              *(u32x2*)(tb + (ln & 31) * 144 + (32 * jj + 8 * v4 + 4 * (ln >> 5)) * 2) =
+                  u32x2{pack_bf16x2(A[4 * v4], A[4 * v4 + 1]), pack_bf16x2(A[4 * v4 + 2], A[4 * v4 + 3])};
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *(f32x4*)(dst + (8 * q) * 512 + 32 * j) = *(const f32x4*)(tb + (8 * q + trow) * 144 + 16 * tchunk);
+            *(u32x4*)(dst + (8 * q) * 512 + 32 * j) = *(const u32x4*)(tb + (8 * q + trow) * 144 + 16 * tchunk);
         }
       }
       if (ln < 32) *(f32x2*)(a.ws_ml + ((int64_t)(w + b) * H + h0 + wave * 32 + ln) * 2) = f32x2{m_run, l_tot};

@@ -98,6 +98,7 @@ void k_partial_small(PartialArgs a) {
       if (threadIdx.x == 0) {
         a.ws_prefix[0] = 0;
         a.ws_prefix[1] = NT;
+        a.ws_prefix[2] = kPartF32;
       }
       for (int i = threadIdx.x; i < H; i += blockDim.x) a.ws_cnt[i] = 0;
     }
@@ -105,6 +106,7 @@ void k_partial_small(PartialArgs a) {
     build_tile_prefix(a.seq_lens, a.B, P, Ls);
     if (blockIdx.x == 0 && blockIdx.y == 0) {
       for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_prefix[i] = P[i];
+      if (threadIdx.x == 0) a.ws_prefix[a.B + 1] = kPartF32;
       for (int i = threadIdx.x; i < H; i += blockDim.x) a.ws_cnt[i] = 0;
     }
     NT = P[a.B];

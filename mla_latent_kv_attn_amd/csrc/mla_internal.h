@@ -35,9 +35,9 @@ struct PartialArgs {
   int B, H, d_c, d_R;
   int W;                        // partial-pass workgroups requested
   float sl2;                    // softmax scale * log2(e)
-  float* ws_acc;                // [slots, H, d_c]
+  float* ws_acc;                // [slots, H, d_c] sums, float or bf16 (kPartF32 / kPartBF16)
   float* ws_ml;                 // [slots, H, 2]   (m in log2 units, l)
-  int* ws_prefix;               // [B + 1] tile prefix sums (written by workgroup 0)
+  int* ws_prefix;               // [B + 2] tile prefix sums, then the format of ws_acc (workgroup 0)
   int* ws_cnt;                  // [H] counters of the fused combine + uv pass, zeroed by workgroup 0
   const void* warm;             // optional: buffer to pull into the cache with the spare workgroups
   int64_t warm_bytes;
@@ -50,14 +50,21 @@ struct CombineArgs {
   const int32_t* seq_lens;
   int B, H, d_c;
   int W;
-  const float* ws_acc;
+  const float* ws_acc;          // float or bf16 elements: ws_prefix[B + 1] says which
   const float* ws_ml;
-  const int* ws_prefix;         // [B + 1] tile prefix sums from the partial pass
+  const int* ws_prefix;         // [B + 2] tile prefix sums and the sums' format, from the partial pass
   int* ws_cnt;                  // [H] fused combine + uv: finished quarters per head (0 on entry)
   float* ws_uv;                 // [min(B, 4), H, 4, 128] fused combine + uv: per-quarter outputs
   float* o_latent;              // [B, H, d_c]
   float* lse;                   // [B, H] or nullptr
 };
+
+// Element type of the partial sums in the acc block, recorded by the partial pass at
+// ws_prefix[B + 1] for the combine: the large-batch MFMA kernel stores bf16 (half the bytes
+// written and read back; the rounding is far below the bf16 operands' own), the fp32 and the
+// small-batch kernels store float.
+constexpr int kPartF32 = 0;
+constexpr int kPartBF16 = 1;
 
 // workspace layout (bytes): acc block, then (m, l) block, then the tile prefix sums, then the
 // counters and per-quarter outputs of the fused combine + uv pass, each 256-byte aligned.  A slot
@@ -72,7 +79,7 @@ inline size_t ws_ml_bytes(int W, int B, int H) {
   size_t b = ws_slots(W, B) * (size_t)H * 2 * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
-inline size_t ws_prefix_bytes(int B) { return (((size_t)B + 1) * sizeof(int) + 255) & ~(size_t)255; }
+inline size_t ws_prefix_bytes(int B) { return (((size_t)B + 2) * sizeof(int) + 255) & ~(size_t)255; }
 inline size_t ws_cnt_bytes(int H) { return ((size_t)H * sizeof(int) + 255) & ~(size_t)255; }
 inline size_t ws_uv_bytes(int B, int H) {
   const size_t nb = B < 4 ? (size_t)B : 4;
@@ -122,6 +129,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define MLA_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// four consecutive partial sums starting at element e (a multiple of 4) of the acc block, stored
+// as float (BF = false) or bf16 (BF = true)
+template <bool BF>
+__device__ __forceinline__ float4 load_part4(const float* acc, int64_t e) {
+  if constexpr (BF) {
+    const u32x2 r = *(const u32x2*)((const uint16_t*)acc + e);
+    return make_float4(__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                       __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u));
+  } else {
+    return *(const float4*)(acc + e);
+  }
+}
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

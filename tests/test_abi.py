@@ -58,7 +58,7 @@ def test_workspace_size_formula(lib):
         slots = W + B - 1
         acc = (slots * H * d_c * 4 + 255) // 256 * 256
         ml = (slots * H * 2 * 4 + 255) // 256 * 256
-        prefix = ((B + 1) * 4 + 255) // 256 * 256
+        prefix = ((B + 2) * 4 + 255) // 256 * 256   # tile prefix sums and the partial sums' format
         cnt = (H * 4 + 255) // 256 * 256
         uv = (min(B, 4) * H * 4 * 128 * 4 + 255) // 256 * 256
         assert ws(B, H, d_c, N, S) == acc + ml + prefix + cnt + uv
