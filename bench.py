@@ -125,8 +125,8 @@ def parse():
     ap.add_argument("--rotate-mb", type=float, default=1024.0, help="bytes of input copies rotated per pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0 = skip)")
     ap.add_argument("--kernel-reps", type=int, default=50, help="events-bracketed passes per kernel")
-    ap.add_argument("--kernel-b2b", action="store_true",
-                    help="also time each call of a several-call step over back-to-back launches of it alone")
+    ap.add_argument("--kernel-in-step", action="store_true",
+                    help="also time each call of a several-call step inside whole steps (an event pair per call)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--row", choices=["decode", "append", "mha", "query", "out", "layer"], default="decode",
                     help="decode: the absorbed decode step (default); append: the cache write of one step; "
@@ -365,12 +365,12 @@ def main():
     torch.cuda.synchronize()
     got = {"o": step.out.cpu().numpy().astype(np.float64), "o_lat": step.o_latent.cpu().numpy().astype(np.float64)}
 
-    # ---------------- per-kernel durations, HIP events on the launch stream, rotating input copies
-    # (weights and caches stay cold).  A one-launch step is timed over kernel_reps back-to-back
-    # launches.  A step of several calls is timed as kernel_reps whole steps in a row with an event
-    # pair around each call, so that every kernel runs where it runs in the timed steps, behind the
-    # others: the chip holds its power limit during the large-batch steps, and a loop of the partial
-    # pass alone runs it at a lower clock than the steps do (--kernel-b2b adds those figures).
+    # ---------------- per-kernel durations: HIP events around kernel_reps back-to-back launches of
+    # one kernel (rotating input copies, so weights and caches stay cold), on the launch stream.
+    # --kernel-in-step adds, for a step of several calls, kernel_reps whole steps in a row with an
+    # event pair around each call: the chip holds its power limit during the large-batch steps,
+    # and a loop of the partial pass alone runs it at a lower clock than the steps do (each event
+    # pair adds a few microseconds of its own).
     single = one_launch_step(wl, args.num_splits)
     if single:
         names = ["step"]
@@ -412,11 +412,11 @@ def main():
         kb.synchronize()
         return ka.elapsed_time(kb) * 1e3 / reps
 
-    kern_us, kern_b2b = {}, {}
+    kern_us, kern_in_step = {}, {}
     with torch.cuda.stream(stream):
-        if single:
-            kern_us["step"] = back_to_back("step")
-        else:
+        for name in names:
+            kern_us[name] = back_to_back(name)
+        if args.kernel_in_step and not single:
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
             torch.cuda._sleep(20_000_000)
             for r in range(reps):
@@ -426,10 +426,7 @@ def main():
                     ev[r][k + 1].record(stream)
             ev[-1][-1].synchronize()
             for k, name in enumerate(names):
-                kern_us[name] = float(np.mean([ev[r][k].elapsed_time(ev[r][k + 1]) for r in range(reps)])) * 1e3
-            if args.kernel_b2b:
-                for name in names:
-                    kern_b2b[name] = back_to_back(name)
+                kern_in_step[name] = float(np.mean([ev[r][k].elapsed_time(ev[r][k + 1]) for r in range(reps)])) * 1e3
     torch.cuda.synchronize()
     if single:
         err = int(step.workspace[:4].view(torch.int32)[0].item())
@@ -471,7 +468,6 @@ def main():
         "hbm_TBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e12, 3),
         "step_alg_bytes": step_bytes,
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "kernels_timing": "back to back" if single else "inside whole steps, an event pair around each call",
         "kernels_frac_of_hbm_peak": {k: round(ab[k] / (kern_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4) for k in names},
         "mfma_util_algorithmic": {"kernel": kname,
                                   "frac_of_bf16_peak": round(af[mfma_name] / (kern_us[mfma_name] * 1e-6) / 1e12
@@ -479,8 +475,8 @@ def main():
         "roofline": roofline,
         "env": environment(),
     }
-    if kern_b2b:
-        out["kernels_us_back_to_back"] = {k: round(v, 3) for k, v in kern_b2b.items()}
+    if kern_in_step:
+        out["kernels_us_in_step"] = {k: round(v, 3) for k, v in kern_in_step.items()}
     print("[bench] checking the timed run's outputs against the oracle", file=sys.stderr, flush=True)
     out["rel_l2_sampled"] = sampled_parity(inp, got)
     if args.cpu_seconds > 0:
