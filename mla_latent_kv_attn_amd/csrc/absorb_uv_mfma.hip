@@ -13,7 +13,8 @@ namespace mla {
 
 // ---------------------------------------------------------------------------------------------
 // absorb.  Grid (H, 2 column halves, ceil(B/128)), 256 threads.  The workgroup stages its
-// [128 x 256] slice of W_UK[h] in LDS; wave w computes rows b0 + 32w .. +31 of the output.
+// [128 x 256] slice of W_UK[h] in LDS; its (32-row block, 32-column block) output tiles are dealt
+// to the four waves.
 // MFMA operand A = q_C rows (k = i contiguous in memory), operand B = W_UK[h][i][col] read with
 // the transposing LDS load ds_read_b64_tr_b16 (the reduction index i is the row index of W_UK).
 // ---------------------------------------------------------------------------------------------
@@ -26,13 +27,19 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const ui
   __shared__ __attribute__((aligned(16))) uint16_t Ws[128 * kAbsStride];
   const int h = blockIdx.x, half = blockIdx.y, bz = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Output tiles: (row block of 32 batch rows, column block of 32), nrb x 8 of them.  The waves
+  // split evenly over the row blocks (4 / nrb waves each; with three row blocks the fourth wave
+  // idles) and a row block's column blocks over its waves, so that every wave has MFMA work at
+  // any batch size; a wave takes its column blocks two at a time (two independent chains).
+  const int nrb = min(4, (B - bz * 128 + 31) / 32);
+  const int wpr = nrb == 1 ? 4 : nrb == 2 ? 2 : 1;   // waves per row block
+  const int rb = wave / wpr, c0 = wave % wpr;
 
   // all 16 loads of the thread's share of the slice go out before the first LDS store (one memory
   // round trip, not one per group), and so do the q rows (rows past B read the last one; their
   // outputs are not stored)
   const uint16_t* wsrc = w + (int64_t)h * 128 * 512 + half * 256;
-  const int b0 = bz * 128 + wave * 32;
-  const int brow = min(b0 + (lane & 31), B - 1), kh = lane >> 5;
+  const int brow = min(bz * 128 + 32 * rb + (lane & 31), B - 1), kh = lane >> 5;
   u32x4 aq[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) aq[ks] = *(const u32x4*)(q + ((int64_t)brow * H + h) * 128 + 16 * ks + 8 * kh);
@@ -49,11 +56,10 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const ui
     *(u32x4*)(&Ws[row * kAbsStride + ch * 8]) = wv[i];
   }
   __syncthreads();
-  if (b0 >= B) return;
+  if (rb >= nrb) return;
   const int G = lane >> 4, r4 = (lane & 15) >> 2, q4 = lane & 3;
-  uint16_t* orow = out + (int64_t)h * 512 + half * 256 + (lane & 31);
-#pragma unroll 1
-  for (int cb = 0; cb < 8; ++cb) {
+  uint16_t* ocol = out + (int64_t)h * 512 + half * 256 + (lane & 31);
+  auto column_block = [&](int cb) __attribute__((always_inline)) -> f32x16 {
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -64,11 +70,21 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const ui
       const u32x4 bop = {l2[0], l2[1], h2[0], h2[1]};
       acc = mfma32x32x16(aq[ks], bop, acc);
     }
+    return acc;
+  };
+  auto store_block = [&](const f32x16& acc, int cb) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int b = b0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (b < B) orow[(int64_t)b * H * 512 + 32 * cb] = (uint16_t)(pack_bf16x2(acc[v], 0.f) & 0xffffu);
+      const int b = bz * 128 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (b < B) ocol[(int64_t)b * H * 512 + 32 * cb] = (uint16_t)(pack_bf16x2(acc[v], 0.f) & 0xffffu);
     }
+  };
+#pragma unroll 1
+  for (int cb = c0; cb < 8; cb += 2 * wpr) {
+    const f32x16 acc1 = column_block(cb);
+    const f32x16 acc2 = column_block(cb + wpr);
+    store_block(acc1, cb);
+    store_block(acc2, cb + wpr);
   }
 }
 
@@ -155,8 +171,11 @@ hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// uv.  Grid (H, ceil(B/32)), 256 threads.  The workgroup computes all 128 output rows of head h
-// for batch rows b0 .. b0+31: wave w takes output rows 32w .. 32w+31.  Operand A = o_lat rows,
+// uv.  Grid (H, ceil(B/32), RS), 256 threads.  With RS = 1 the workgroup computes all 128 output
+// rows of head h for batch rows b0 .. b0+31: wave w takes output rows 32w .. 32w+31.  With RS = 2
+// (fewer workgroups than CUs otherwise) workgroup (h, ., r) computes output rows 64r .. 64r+63:
+// waves w and w + 2 take rows 64r + 32w .. +31 over the two halves of the k range, and wave w + 2
+// hands its sum to wave w through LDS.  Operand A = o_lat rows,
 // fp32 split into bf16 hi + bf16 lo (the product keeps ~16 mantissa bits of o_lat); the split is
 // done once per workgroup into LDS (32 rows x 512 columns x 2 halves, 64 KiB), where every wave
 // reads it.  Operand B = W_UV[h][i][k] rows straight from global memory (k contiguous).
@@ -173,20 +192,24 @@ __device__ __forceinline__ void split_hi_lo(const float4& x0, const float4& x1, 
 
 constexpr int kUvRow = 1024 + 16;   // LDS bytes per o_lat row and half (512 bf16 + pad)
 
+template <int RS>
 __global__ __launch_bounds__(256) void k_uv_bf16(const float* __restrict__ o_lat, const uint16_t* __restrict__ w,
                                                  float* __restrict__ out, int B, int H) {
+  constexpr int KS = 32 / RS;   // k-steps per wave
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][32 * kUvRow];   // [hi/lo][row][k]
-  const int h = blockIdx.x, bz = blockIdx.y;
+  __shared__ f32x4 red[RS == 2 ? 2 * 4 * 64 : 1];   // RS = 2: the k-half partials of waves 2 and 3
+  const int h = blockIdx.x, bz = blockIdx.y, rs = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b0 = bz * 32;
-  const int i0 = wave * 32;
+  const int i0 = RS == 1 ? wave * 32 : 64 * rs + 32 * (wave & 1);
+  const int k0 = RS == 1 ? 0 : KS * (wave >> 1);
   const int kh = lane >> 5;
-  // this wave's 32 weight rows for all 32 k-steps, loaded before anything waits (one memory
+  // this wave's 32 weight rows for its KS k-steps, loaded before anything waits (one memory
   // round trip for the whole workgroup, together with the o_lat rows below)
-  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh;
-  u32x4 bw[32];
+  const uint16_t* wr = w + ((int64_t)h * 128 + i0 + (lane & 31)) * 512 + 8 * kh + 16 * k0;
+  u32x4 bw[KS];
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) bw[ks] = *(const u32x4*)(wr + 16 * ks);
+  for (int ks = 0; ks < KS; ++ks) bw[ks] = *(const u32x4*)(wr + 16 * ks);
   // stage: thread t converts 8 consecutive columns (8 (t % 64) ..) of rows t / 64 + 4 j
   float4 xv[16];
 #pragma unroll
@@ -207,21 +230,39 @@ __global__ __launch_bounds__(256) void k_uv_bf16(const float* __restrict__ o_lat
     *(u32x4*)(xs[1] + r * kUvRow + 16 * lane) = lo;
   }
   __syncthreads();
-  const uint8_t* ahi = xs[0] + (lane & 31) * kUvRow + 16 * kh;
-  const uint8_t* alo = xs[1] + (lane & 31) * kUvRow + 16 * kh;
+  const uint8_t* ahi = xs[0] + (lane & 31) * kUvRow + 16 * kh + 32 * k0;
+  const uint8_t* alo = xs[1] + (lane & 31) * kUvRow + 16 * kh + 32 * k0;
   f32x16 acc = {}, acc2 = {};
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const u32x4 hi = *(const u32x4*)(ahi + 32 * ks);
     const u32x4 lo = *(const u32x4*)(alo + 32 * ks);
     acc = mfma32x32x16(hi, bw[ks], acc);
     acc2 = mfma32x32x16(lo, bw[ks], acc2);
   }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] += acc2[v];
+  if constexpr (RS == 2) {
+    // waves 2 and 3 hand their half of the k range to waves 0 and 1 (same output rows)
+    if (wave >= 2) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        red[((wave - 2) * 4 + v4) * 64 + lane] = f32x4{acc[4 * v4], acc[4 * v4 + 1], acc[4 * v4 + 2], acc[4 * v4 + 3]};
+    }
+    __syncthreads();
+    if (wave >= 2) return;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const f32x4 o = red[(wave * 4 + v4) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * v4 + e] += o[e];
+    }
+  }
   float* orow = out + (int64_t)h * 128 + i0 + (lane & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int b = b0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (b < B) orow[(int64_t)b * H * 128] = acc[v] + acc2[v];
+    if (b < B) orow[(int64_t)b * H * 128] = acc[v];
   }
 }
 
@@ -480,8 +521,14 @@ hipError_t launch_uv_bf16(const float* o_lat, const void* w, float* out, int B, 
       hipLaunchKernelGGL(k_uv_gemv<4>, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
     return hipGetLastError();
   }
-  dim3 grid(H, (B + 31) / 32);
-  hipLaunchKernelGGL(k_uv_bf16, grid, dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+  // with fewer workgroups than CUs, the output rows of a head are split over two workgroups, each
+  // wave pair taking half of the k range (half the weight bytes per CU)
+  const int nbz = (B + 31) / 32;
+  if ((int64_t)H * nbz < 256) {
+    hipLaunchKernelGGL(k_uv_bf16<2>, dim3(H, nbz, 2), dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+  } else {
+    hipLaunchKernelGGL(k_uv_bf16<1>, dim3(H, nbz, 1), dim3(256), 0, s, o_lat, (const uint16_t*)w, out, B, H);
+  }
   return hipGetLastError();
 }
 

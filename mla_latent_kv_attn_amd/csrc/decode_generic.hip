@@ -150,7 +150,8 @@ hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
 // Grid (H, B, d_c / 128), 256 threads: the workgroup merges 128 columns.  The (m, l) pairs are
 // reduced by the whole workgroup and the segment weights 2^(m_s - M) kept in LDS (the first
 // kCombW of them); thread t then takes float4 column group t % 32 and segments t / 32 + 8 i,
-// four loads in flight, and the 8 segment groups are summed through LDS.
+// four loads in flight (the first four issued before the reduction), and the 8 segment groups
+// are summed through LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int kCombW = 1024;
 
@@ -186,6 +187,18 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
   const int w1 = (int)(((int64_t)Pb1 * Wp + NT - 1) / NT) - 1;
   const int nseg = w1 - w0 + 1;
   const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml + H s
+  const int64_t e0 = ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at element e0 + H d_c s
+  const int64_t astride = (int64_t)H * d_c;
+  // Thread t takes segments t / 32 + 8 u.  Its first four (u = 0..3) do not depend on the weights:
+  // their loads go out before the (m, l) reduction, so that both wait on one memory round trip.
+  // Segments past nseg read the last one and get weight 0 (a load per remaining segment would be
+  // waited on one by one).
+  const bool has_col = col < d_c;
+  float4 v0[4];
+  if (has_col) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v0[u] = load_part4<BF>(a.ws_acc, e0 + min(sg + 8 * u, nseg - 1) * astride);
+  }
   float mloc = -INFINITY;
   for (int s = tid; s < nseg; s += 256) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
   const float M = block_reduce256(mloc, true, rr);
@@ -200,16 +213,8 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
   auto weight = [&](int s) -> float { return s < kCombW ? wts[s] : exp2f(ml[(int64_t)s * H].x - M); };
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (col < d_c) {
-    const int64_t e0 = ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at element e0 + H d_c s
-    const int64_t astride = (int64_t)H * d_c;
-    // four segments per pass, all four loads in flight together; in the last pass segments past
-    // nseg read the last one and get weight 0 (a load per remaining segment would be waited on
-    // one by one)
-    for (int s = sg; s < nseg; s += 32) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_part4<BF>(a.ws_acc, e0 + min(s + 8 * u, nseg - 1) * astride);
+  if (has_col) {
+    auto accumulate = [&](const float4 (&v)[4], int s) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float f = s + 8 * u < nseg ? weight(s + 8 * u) : 0.f;
@@ -218,6 +223,14 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
         o.z = fmaf(f, v[u].z, o.z);
         o.w = fmaf(f, v[u].w, o.w);
       }
+    };
+    accumulate(v0, sg);
+    // further passes of four segments (more than 32 segments), all four loads in flight together
+    for (int s = sg + 32; s < nseg; s += 32) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load_part4<BF>(a.ws_acc, e0 + min(s + 8 * u, nseg - 1) * astride);
+      accumulate(v, s);
     }
   }
   red[sg][c4] = o;
@@ -252,9 +265,9 @@ constexpr int kCombWB = 128;   // segments whose weights are kept in LDS (the re
 
 // Combine for batches wide enough to fill the chip with one workgroup per (32-head block,
 // sequence): grid (H/32, B), 256 threads.  The (m, l) reduction is done once per head block; the
-// block's 32 partial rows are 64 KiB contiguous per segment, which thread t reads as float4
-// t + 256 i (i = 0..15: head 2i + t / 128, columns 4 (t % 128) ..), sixteen loads in flight.
-// d_c must be 512.
+// block's 32 partial rows are contiguous per segment (64 KiB as float, 32 KiB as bf16); thread t
+// reads groups of four sums t + 256 i (i = 0..15: head 2i + t / 128, columns 4 (t % 128) ..),
+// sixteen loads in flight, the first segment's during the reduction.  d_c must be 512.
 template <bool BF>
 __device__ __forceinline__ void combine_heads(const CombineArgs& a, float (*red)[32], float* Ms, float* Lsum,
                                               float (*wts)[32]) {

@@ -257,10 +257,13 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(step.out, eager)
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 33, 129])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 33, 70, 129, 200])
 def test_projections_batch_sweep(B):
     """The two projections alone at batch sizes on both sides of the small-batch switch (B <= 4
-    streams the weights, larger batches use MFMA tiles of 128 / 32 rows), fed the oracle's o_lat."""
+    streams the weights, larger batches use MFMA tiles of 128 / 32 rows), fed the oracle's o_lat.
+    The MFMA absorb meets one to four 32-row blocks per workgroup (three at B = 70 and in the
+    second workgroup row of B = 200); W_UV splits a head's rows over two workgroups when the grid
+    would not fill the chip (B = 5, and the 32-head cases)."""
     wl = WORKLOADS[2].with_(name=f"proj-b{B}", B=B, H=128 if B <= 33 else 32, n_max=40, len_lo=1, len_hi=40)
     inp = make_inputs(wl)
     ref = oracle.decode(inp)
