@@ -94,22 +94,38 @@ def cmd_stats(a):
         for (name, grid), v in grp.items():
             lines.append(f"| {name} | {grid} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} |")
     if a.trace and bench and not a.by_grid:
-        # the bench's per-kernel timing loop is the last kernel_reps dispatches of each kernel
+        # dispatch order in a bench.py run: the steps (warm-up, graph replays, spread replays), then
+        # kernel_reps back-to-back launches of each kernel, then (--kernel-in-step) kernel_reps whole
+        # steps with an event pair around each call
+        in_step = "kernels_us_in_step" in bench
         disp = {}
         for r in _rows(a.trace):
             name = _col(r, "Kernel_Name").split("(")[0].replace("void ", "")
             disp.setdefault(name, []).append((int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp"))))
-        lines += ["", f"Average over the last {a.loop} dispatches of each kernel (the bench's events-timed loop; "
-                      "the table above also counts the graph-replayed steps):", ""]
+        L = a.loop
+        mean_us = lambda v: f"{statistics.mean(e - s_ for s_, e in v) / 1e3:.2f}" if v else "-"
+        lines += ["", "Average duration per launch (us) by part of the run: the steps (graph replays and warm-up), "
+                      f"the bench's {L} back-to-back launches of the kernel alone" +
+                      (f", and its {L} whole steps with an event pair per call" if in_step else "") + ":", "",
+                  "| kernel | steps | back to back |" + (" in steps, events |" if in_step else ""),
+                  "|---|---|---|" + ("---|" if in_step else "")]
         for name, v in disp.items():
             if not name.startswith("mla::"):
                 continue
             v.sort()
-            tail = v[-a.loop:]
-            lines.append(f"    {name}: {statistics.mean(e - s_ for s_, e in tail) / 1e3:.2f} us")
+            if in_step:
+                steps, b2b, ins = v[:-2 * L], v[-2 * L:-L], v[-L:]
+                lines.append(f"| {name} | {mean_us(steps)} | {mean_us(b2b)} | {mean_us(ins)} |")
+            else:
+                steps, b2b = v[:-L], v[-L:]
+                lines.append(f"| {name} | {mean_us(steps)} | {mean_us(b2b)} |")
     if bench:
         if "kernels_us" in bench:
-            lines += ["", "bench.py line of the same run (HIP-event averages, us): " + json.dumps(bench["kernels_us"])]
+            lines += ["", "bench.py line of the same run (HIP-event averages, us; back to back): " +
+                      json.dumps(bench["kernels_us"])]
+            if "kernels_us_in_step" in bench:
+                lines += ["bench.py, in whole steps with an event pair per call (us): " +
+                          json.dumps(bench["kernels_us_in_step"])]
         else:
             lines += ["", "bench.py line of the same run:"]
         lines += [f"ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "

@@ -327,6 +327,52 @@ def test_step_with_fused_combine_uv(name, splits):
     compare(inp, got, oracle.decode(inp))
 
 
+WIDE_STEP = {
+    # large-batch partial pass (bf16 sums), packed cache, 40 sequences
+    "packed-40": (mini(3, name="wide-packed", B=40, n_max=1100, len_lo=1, len_hi=1100), 0, 1),
+    # paged cache, 20 sequences (W_UV over two workgroups per head)
+    "paged-20": (mini(4, name="wide-paged", B=20, n_max=1856, len_lo=1, len_hi=1856), 0, 2),
+    # E4M3 cache (large-batch partial at any batch), 6 sequences
+    "fp8-6": (mini(5, name="wide-fp8", B=6, n_max=300, len_lo=1, len_hi=300), 0, 3),
+    # about 200 segments per sequence (more than the combines keep weights for in LDS)
+    "many-segments": (mini(2, name="wide-segs", B=5, n_max=8192, len_lo=1, len_hi=8192), 1000, 4),
+    # small-batch partial pass (float sums) at B > 4
+    "small-f32-sums": (mini(2, name="wide-small", B=12, n_max=640, len_lo=1, len_hi=640), 0, 5),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_STEP))
+def test_step_wide_batch(name):
+    """The decode step at B > 4 (absorb, partial, combine, W_UV): bf16 and float partial sums,
+    packed, paged and E4M3 caches, empty sequences, a sequence of one token, and many segments
+    per sequence.  Sampled comparison (all pairs for the small cases)."""
+    wl, splits, seed = WIDE_STEP[name]
+    rng = np.random.default_rng(100 + seed)
+    lens = rng.integers(1, wl.n_max + 1, size=wl.B)
+    lens[:3] = [0, wl.n_max, 1]
+    if name == "many-segments":
+        lens[:] = wl.n_max
+        lens[0] = 0
+    inp = make_inputs(wl, lens=lens)
+    got = run_step(inp, num_splits=splits)
+    all_finite(got, inp)
+    if wl.B * wl.n_max <= 4096:
+        compare(inp, got, oracle.decode(inp))
+    else:
+        pairs = _sample_pairs(inp)
+        compare(inp, got, oracle.decode(inp, pairs=pairs), pairs=pairs)
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_size_step_sampled(cfg):
+    """The full-size batched workloads through the decode step, as the benchmark runs them."""
+    inp = make_inputs(cfg)
+    got = run_step(inp)
+    all_finite(got, inp)
+    pairs = _sample_pairs(inp)
+    compare(inp, got, oracle.decode(inp, pairs=pairs), pairs=pairs)
+
+
 def test_step_v3_b1_full():
     inp = make_inputs(2)
     got = run_step(inp)
