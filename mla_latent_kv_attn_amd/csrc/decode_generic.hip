@@ -147,11 +147,11 @@ hipError_t launch_partial_f32(const PartialArgs& a, hipStream_t s) {
 // The segments of sequence b are the partial-pass workgroups w0..w1 whose tile ranges meet b's
 // tiles (tile prefix sums left in the workspace by the partial pass, followed by the element
 // type of its sums, float or bf16).
-// Grid (H, B, d_c / 128), 256 threads: the workgroup merges 128 columns.  The (m, l) pairs are
-// reduced by the whole workgroup and the segment weights 2^(m_s - M) kept in LDS (the first
-// kCombW of them); thread t then takes float4 column group t % 32 and segments t / 32 + 8 i,
-// four loads in flight (the first four issued before the reduction), and the 8 segment groups
-// are summed through LDS.
+// Grid (H, B, ceil(d_c / 512)), 256 threads: the workgroup merges up to 512 columns of one row.
+// The (m, l) pairs are reduced by the whole workgroup and the segment weights 2^(m_s - M) kept in
+// LDS (the first kCombW of them); thread t takes float4 column group t % 128 and segments
+// t / 128 + 2 i, sixteen loads in flight (the first sixteen issued before the reduction), and the
+// two segment groups are summed through LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int kCombW = 1024;
 
@@ -169,11 +169,12 @@ __device__ __forceinline__ float block_reduce256(float v, bool is_max, float* re
 }
 
 template <bool BF>
-__device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)[33], float* wts, float* rr) {
+__device__ __forceinline__ void combine_rows(const CombineArgs& a, float4* red, float* wts, float* rr) {
+  constexpr int NU = 16;   // segments per thread loaded before the (m, l) reduction (32 per row)
   const int h = blockIdx.x, b = blockIdx.y, cq = blockIdx.z, tid = threadIdx.x;
   const int d_c = a.d_c, H = a.H;
-  const int c4 = tid & 31, sg = tid >> 5;
-  const int col = cq * 128 + 4 * c4;
+  const int c4 = tid & 127, sg = tid >> 7;
+  const int col = cq * 512 + 4 * c4;
   const int Pb = a.ws_prefix[b], Pb1 = a.ws_prefix[b + 1], NT = a.ws_prefix[a.B];
   float* out = a.o_latent + ((int64_t)b * H + h) * d_c;
   if (Pb1 == Pb) {
@@ -189,22 +190,25 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
   const float2* ml = (const float2*)(a.ws_ml + ((int64_t)(w0 + b) * H + h) * 2);   // segment s at ml + H s
   const int64_t e0 = ((int64_t)(w0 + b) * H + h) * d_c + col;   // segment s at element e0 + H d_c s
   const int64_t astride = (int64_t)H * d_c;
-  // Thread t takes segments t / 32 + 8 u.  Its first four (u = 0..3) do not depend on the weights:
-  // their loads go out before the (m, l) reduction, so that both wait on one memory round trip.
-  // Segments past nseg read the last one and get weight 0 (a load per remaining segment would be
-  // waited on one by one).
+  // Thread t takes segments t / 128 + 2 u.  Its first NU do not depend on the weights: their loads
+  // go out before the (m, l) reduction, so that both wait on one memory round trip.  Segments
+  // past nseg read the last one and get weight 0 (a load per remaining segment would be waited on
+  // one by one; skipping them behind a branch measured slower).
   const bool has_col = col < d_c;
-  float4 v0[4];
+  float4 v0[NU];
   if (has_col) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v0[u] = load_part4<BF>(a.ws_acc, e0 + min(sg + 8 * u, nseg - 1) * astride);
+    for (int u = 0; u < NU; ++u) v0[u] = load_part4<BF>(a.ws_acc, e0 + min(sg + 2 * u, nseg - 1) * astride);
   }
-  float mloc = -INFINITY;
-  for (int s = tid; s < nseg; s += 256) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
+  // (m, l) of segment tid is kept in registers between the two reductions (segments past 256,
+  // a rare case, are read again)
+  const float2 ml_t = tid < nseg ? ml[(int64_t)tid * H] : make_float2(-INFINITY, 0.f);
+  float mloc = ml_t.x;
+  for (int s = tid + 256; s < nseg; s += 256) mloc = fmaxf(mloc, ml[(int64_t)s * H].x);
   const float M = block_reduce256(mloc, true, rr);
   float lloc = 0.f;
   for (int s = tid; s < nseg; s += 256) {
-    const float2 v = ml[(int64_t)s * H];
+    const float2 v = s == tid ? ml_t : ml[(int64_t)s * H];
     const float f = exp2f(v.x - M);
     if (s < kCombW) wts[s] = f;
     lloc += f * v.y;
@@ -214,10 +218,10 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (has_col) {
-    auto accumulate = [&](const float4 (&v)[4], int s) {
+    auto accumulate = [&](const float4 (&v)[NU], int s) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float f = s + 8 * u < nseg ? weight(s + 8 * u) : 0.f;
+      for (int u = 0; u < NU; ++u) {
+        const float f = s + 2 * u < nseg ? weight(s + 2 * u) : 0.f;
         o.x = fmaf(f, v[u].x, o.x);
         o.y = fmaf(f, v[u].y, o.y);
         o.z = fmaf(f, v[u].z, o.z);
@@ -225,34 +229,26 @@ __device__ __forceinline__ void combine_rows(const CombineArgs& a, float4 (*red)
       }
     };
     accumulate(v0, sg);
-    // further passes of four segments (more than 32 segments), all four loads in flight together
-    for (int s = sg + 32; s < nseg; s += 32) {
-      float4 v[4];
+    // further passes (more than 32 segments), all NU loads in flight together
+    for (int s = sg + 2 * NU; s < nseg; s += 2 * NU) {
+      float4 v[NU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_part4<BF>(a.ws_acc, e0 + min(s + 8 * u, nseg - 1) * astride);
+      for (int u = 0; u < NU; ++u) v[u] = load_part4<BF>(a.ws_acc, e0 + min(s + 2 * u, nseg - 1) * astride);
       accumulate(v, s);
     }
   }
-  red[sg][c4] = o;
+  if (sg == 1) red[c4] = o;
   __syncthreads();
-  if (sg == 0 && col < d_c) {
-    float4 t = red[0][c4];
-#pragma unroll
-    for (int g = 1; g < 8; ++g) {
-      const float4 u = red[g][c4];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-    }
+  if (sg == 0 && has_col) {
+    const float4 u = red[c4];
     const float inv = 1.f / Ls;
-    *(float4*)(out + col) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    *(float4*)(out + col) = make_float4((o.x + u.x) * inv, (o.y + u.y) * inv, (o.z + u.z) * inv, (o.w + u.w) * inv);
   }
   if (a.lse && tid == 0 && cq == 0) a.lse[(int64_t)b * H + h] = (M + log2f(Ls)) * 0.69314718055994530942f;
 }
 
 __global__ __launch_bounds__(256) void k_combine_rows(CombineArgs a) {
-  __shared__ float4 red[8][33];
+  __shared__ float4 red[128];
   __shared__ float wts[kCombW];
   __shared__ float rr[4];
   if (a.ws_prefix[a.B + 1] == kPartBF16)
@@ -295,8 +291,10 @@ __device__ __forceinline__ void combine_heads(const CombineArgs& a, float (*red)
   float4 x0[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) x0[i] = load_part4<BF>(a.ws_acc, src + (r0 + 2 * i) * d_c);
-  float mloc = -INFINITY;
-  for (int s = g; s < nseg; s += 8) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
+  // (m, l) of segment g is kept in registers between the two reductions
+  const float2 ml_g = g < nseg ? ml[(int64_t)g * H + hr] : make_float2(-INFINITY, 0.f);
+  float mloc = ml_g.x;
+  for (int s = g + 8; s < nseg; s += 8) mloc = fmaxf(mloc, ml[(int64_t)s * H + hr].x);
   red[g][hr] = mloc;
   __syncthreads();
   if (tid < 32) {
@@ -310,7 +308,7 @@ __device__ __forceinline__ void combine_heads(const CombineArgs& a, float (*red)
     const float M = Ms[hr];
     float lloc = 0.f;
     for (int s = g; s < nseg; s += 8) {
-      const float2 q = ml[(int64_t)s * H + hr];
+      const float2 q = s == g ? ml_g : ml[(int64_t)s * H + hr];
       const float f = exp2f(q.x - M);
       if (s < kCombWB) wts[s][hr] = f;
       lloc += f * q.y;
@@ -368,7 +366,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.H % 32 == 0 && a.d_c == 512 && (int64_t)(a.H / 32) * a.B >= 256)
     hipLaunchKernelGGL(k_combine_heads, dim3(a.H / 32, a.B), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_combine_rows, dim3(a.H, a.B, (a.d_c + 127) / 128), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_combine_rows, dim3(a.H, a.B, (a.d_c + 511) / 512), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
