@@ -22,18 +22,21 @@ constexpr int kAbsStride = 256 + 16;  // LDS row stride (bf16 elements): 544 B =
 
 // (q is not __restrict__: an invariant load could be sunk below the LDS stores and the barrier,
 // which costs a second memory round trip)
+template <bool STG>
 __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const uint16_t* __restrict__ w,
                                                      uint16_t* __restrict__ out, int B, int H) {
   __shared__ __attribute__((aligned(16))) uint16_t Ws[128 * kAbsStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ostg[STG ? 4 : 1][32 * 144];   // per wave: 32 rows x 64 bf16 + pad
   const int h = blockIdx.x, half = blockIdx.y, bz = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Output tiles: (row block of 32 batch rows, column block of 32), nrb x 8 of them.  The waves
   // split evenly over the row blocks (4 / nrb waves each; with three row blocks the fourth wave
   // idles) and a row block's column blocks over its waves, so that every wave has MFMA work at
-  // any batch size; a wave takes its column blocks two at a time (two independent chains).
+  // any batch size; a wave takes two adjacent column blocks at a time (two independent chains,
+  // and 128-byte output rows).
   const int nrb = min(4, (B - bz * 128 + 31) / 32);
   const int wpr = nrb == 1 ? 4 : nrb == 2 ? 2 : 1;   // waves per row block
-  const int rb = wave / wpr, c0 = wave % wpr;
+  const int rb = wave / wpr, cpw = 8 / wpr, cfirst = (wave % wpr) * cpw;
 
   // all 16 loads of the thread's share of the slice go out before the first LDS store (one memory
   // round trip, not one per group), and so do the q rows (rows past B read the last one; their
@@ -58,7 +61,6 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const ui
   __syncthreads();
   if (rb >= nrb) return;
   const int G = lane >> 4, r4 = (lane & 15) >> 2, q4 = lane & 3;
-  uint16_t* ocol = out + (int64_t)h * 512 + half * 256 + (lane & 31);
   auto column_block = [&](int cb) __attribute__((always_inline)) -> f32x16 {
     f32x16 acc = {};
 #pragma unroll
@@ -72,19 +74,42 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const uint16_t* q, const ui
     }
     return acc;
   };
-  auto store_block = [&](const f32x16& acc, int cb) __attribute__((always_inline)) {
+  // lane l holds column l & 31 of rows 8 (v >> 2) + 4 (l >> 5) + (v & 3) of a block.  With a
+  // 16-byte aligned output (STG) the pair of blocks (cb, cb + 1) goes through this wave's staging
+  // rows and leaves as 16-byte pieces of 128-byte output rows, eight rows per store instruction;
+  // otherwise each lane stores its bf16 values one by one.
+  uint8_t* stg = ostg[STG ? wave : 0];
+  auto store_pair = [&](const f32x16& acc1, const f32x16& acc2, int cb) __attribute__((always_inline)) {
+    if constexpr (!STG) {
+      uint16_t* ocol = out + (int64_t)h * 512 + half * 256 + 32 * cb + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int b = bz * 128 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (b < B) {
+          ocol[(int64_t)b * H * 512] = (uint16_t)(pack_bf16x2(acc1[v], 0.f) & 0xffffu);
+          ocol[(int64_t)b * H * 512 + 32] = (uint16_t)(pack_bf16x2(acc2[v], 0.f) & 0xffffu);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int b = bz * 128 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (b < B) ocol[(int64_t)b * H * 512 + 32 * cb] = (uint16_t)(pack_bf16x2(acc[v], 0.f) & 0xffffu);
+      const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      *(uint16_t*)(stg + row * 144 + 2 * (lane & 31)) = (uint16_t)(pack_bf16x2(acc1[v], 0.f) & 0xffffu);
+      *(uint16_t*)(stg + row * 144 + 64 + 2 * (lane & 31)) = (uint16_t)(pack_bf16x2(acc2[v], 0.f) & 0xffffu);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 8 * q + (lane >> 3), b = bz * 128 + 32 * rb + row;
+      const u32x4 piece = *(const u32x4*)(stg + row * 144 + 16 * (lane & 7));
+      if (b < B) *(u32x4*)(out + ((int64_t)b * H + h) * 512 + half * 256 + 32 * cb + 8 * (lane & 7)) = piece;
     }
   };
 #pragma unroll 1
-  for (int cb = c0; cb < 8; cb += 2 * wpr) {
+  for (int cb = cfirst; cb < cfirst + cpw; cb += 2) {
     const f32x16 acc1 = column_block(cb);
-    const f32x16 acc2 = column_block(cb + wpr);
-    store_block(acc1, cb);
-    store_block(acc2, cb + wpr);
+    const f32x16 acc2 = column_block(cb + 1);
+    store_pair(acc1, acc2, cb);
   }
 }
 
@@ -165,8 +190,12 @@ hipError_t launch_absorb_bf16(const void* q, const void* w, void* out, int B, in
     return hipGetLastError();
   }
   dim3 grid(H, 2, (B + 127) / 128);
-  hipLaunchKernelGGL(k_absorb_bf16, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w, (uint16_t*)out,
-                     B, H);
+  if (((uintptr_t)out & 15) == 0)
+    hipLaunchKernelGGL(k_absorb_bf16<true>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
+                       (uint16_t*)out, B, H);
+  else
+    hipLaunchKernelGGL(k_absorb_bf16<false>, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)w,
+                       (uint16_t*)out, B, H);
   return hipGetLastError();
 }
 

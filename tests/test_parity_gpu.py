@@ -284,6 +284,24 @@ def test_projections_batch_sweep(B):
     assert e_q <= 4e-3 and e_o <= 1e-4
 
 
+@pytest.mark.parametrize("B", [5, 70])
+def test_absorb_output_alignment(B):
+    """The MFMA absorb writes 16-byte pieces of whole output rows when q_abs is 16-byte aligned and
+    single bf16 values otherwise: a q_abs that starts 4 bytes into its buffer gets the same bits."""
+    wl = WORKLOADS[2].with_(name=f"absorb-align-b{B}", B=B, n_max=40, len_lo=1, len_hi=40)
+    inp = make_inputs(wl)
+    dev = to_device(inp)
+    print(f"[gpu] absorb alignment B={B}", flush=True)
+    aligned = ops.mla_absorb_q(dev["q_C"], dev["W_UK"])
+    buf = torch.zeros(B * wl.H * wl.d_c + 8, dtype=torch.bfloat16, device="cuda")
+    shifted = buf[2:2 + B * wl.H * wl.d_c].view(B, wl.H, wl.d_c)
+    assert shifted.data_ptr() % 16 == 4
+    ops.mla_absorb_q(dev["q_C"], dev["W_UK"], out=shifted)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned.view(torch.int16), shifted.view(torch.int16))
+    assert torch.count_nonzero(buf[:2].view(torch.int16)) == 0 and torch.count_nonzero(buf[-6:].view(torch.int16)) == 0
+
+
 @pytest.mark.parametrize("H,B,splits", [(128, 64, 0), (128, 64, 200), (64, 128, 300)])
 def test_wide_batch_combine(H, B, splits):
     """Batches wide enough (H/32 * B >= 256) for the combine pass to take one workgroup per
